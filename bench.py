@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE dispatch / combine hot path on one MI355X.
+
+One step = one pass of the whole path over one batch: ep_layout (routing
+layout, two kernels), ep_dispatch (scatter, one kernel) and ep_combine
+(gather-reduce, one kernel), on the 4096-token prefill workload: T=4096,
+H=7168, E=256 experts, top-8 group-limited routing (8 groups of 32, top-4
+groups), bf16 payload, contiguous layout, seed 0.  Inputs are synthetic,
+seeded, and already resident in HBM when the timed region starts.
+
+Prints one JSON line.  `value` is effective GB/s of the whole step:
+algorithmic bytes of dispatch (layout included) plus combine, divided by the
+wall time per step between two device synchronisations.  `roofline` reports
+the dominant kernel against the 8 TB/s HBM peak, with its duration measured
+by HIP events on the stream it runs on.  `cpu_baseline` times the CPU oracle
+on the same inputs (serial, one core).
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 3]
+                  [--no-cpu-baseline] [--cpu-seconds 12]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "dispatch+combine effective GB/s and µs/call, % of HBM peak, 1×MI355X"
+
+
+def algorithmic_bytes(wl, count=None):
+    """Bytes the method must move (each input read once, each output written
+    once), per call.  V = routing entries that get a receive row."""
+    T, H, k, E = wl.T, wl.H, wl.k, wl.E
+    V = T * k if count is None else int(sum(min(c, wl.cap) if wl.cap else c for c in count))
+    p = 1 if wl.fp8 else 2
+    scales = 4 * V * (H // 128) if wl.fp8 else 0
+    R = T * k if wl.cap == 0 else E * wl.cap
+    layout_k = 4 * T * k + 4 * T * k + 4 * R + 4 * (2 * E + 1) + 8
+    dispatch_k = 2 * T * H + 4 * T * k + V * H * p + scales
+    combine_k = 2 * V * H + 4 * T * k + 4 * T * k + 2 * T * H
+    # whole-path totals: intermediate re-reads of slot_of are not counted
+    b_disp = 2 * T * H + 4 * T * k + V * H * p + scales + 4 * T * k + 4 * V + 4 * (2 * E + 1)
+    b_comb = 2 * V * H + 4 * T * k + 4 * T * k + 2 * T * H
+    return dict(V=V, layout_kernels=layout_k, dispatch_kernel=dispatch_k,
+                combine_kernel=combine_k, dispatch_total=b_disp, combine_total=b_comb)
+
+
+def kernel_source_digest(name):
+    path = os.path.join(ROOT, "combine_ep_layout_09_amd", "csrc", name)
+    h = hashlib.sha256()
+    for f in (path, os.path.join(ROOT, "combine_ep_layout_09_amd", "csrc", "ep_device.h")):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, source, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line:
+            key, _, v = line.partition(":")
+            vals[key.strip()] = v.strip()
+    if vals.get("source_digest") != kernel_source_digest(source):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def measure_copy_gbps(torch, nbytes=1 << 30, reps=10):
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(2):
+        b.copy_(a)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    t = s.elapsed_time(e) / 1e3 / reps
+    del a, b
+    return 2 * nbytes / t / 1e9
+
+
+def cpu_baseline(wl, eo_host, bytes_total, target_s):
+    import oracle
+    reps, elapsed = 0, 0.0
+    t_start = time.perf_counter()
+    while reps < 2 or (elapsed < target_s and reps < 50):
+        t0 = time.perf_counter()
+        lay = oracle.layout(wl.topk_idx, wl.E, wl.cap)
+        oracle.dispatch(wl.x, lay["slot_of"], wl.R, wl.fp8)
+        oracle.combine(eo_host, lay["slot_of"], wl.topk_weights, want_acc=False)
+        elapsed += time.perf_counter() - t0
+        reps += 1
+        if time.perf_counter() - t_start > 3 * target_s:
+            break
+    per = elapsed / reps
+    return {"value": round(bytes_total / per / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{reps} full passes (layout+dispatch+combine) of the same workload, "
+                      f"serial C++ oracle, {per * 1e3:.1f} ms per pass"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
+              "supported (the multi-GPU exchange is not part of it)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import combine_ep_layout_09_amd as ep
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
+    wl = workloads.make(args.config)
+    eo_host = wl.expert_out()
+    dev = "cuda"
+    prob = ep.Problem(wl.T, wl.H, wl.k, wl.E, wl.cap, wl.fp8)
+    idx = torch.from_numpy(wl.topk_idx).to(dev)
+    w = torch.from_numpy(wl.topk_weights).to(dev)
+    x = torch.from_numpy(wl.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    eo = torch.from_numpy(eo_host.view(np.int16)).to(dev).view(torch.bfloat16)
+    lay = ep.Layout.empty(prob, dev)
+    ws = ep.alloc_workspace(prob, dev)
+    recv_x, recv_s = ep.alloc_recv(prob, dev)
+    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+    do_layout = ep.prepare_layout(prob, idx, lay, ws)
+    do_dispatch = ep.prepare_dispatch(prob, x, lay, recv_x, recv_s)
+    do_combine = ep.prepare_combine(prob, eo, lay, w, y)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        do_layout(stream)
+        do_dispatch(stream)
+        do_combine(stream)
+
+    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    count = lay.count.cpu().numpy()
+    nb = algorithmic_bytes(wl, count)
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record(stream)
+        do_layout(stream)
+        ev[i][1].record(stream)
+        do_dispatch(stream)
+        ev[i][2].record(stream)
+        do_combine(stream)
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"[bench] timed {K} steps in {wall:.4f} s", file=sys.stderr, flush=True)
+
+    def mean_ms(a, b):
+        return sum(ev[i][a].elapsed_time(ev[i][b]) for i in range(K)) / K
+
+    layout_ms, dispatch_ms, combine_ms = mean_ms(0, 1), mean_ms(1, 2), mean_ms(2, 3)
+    ms_per_step = wall / K * 1e3
+    total_bytes = nb["dispatch_total"] + nb["combine_total"]
+    value = total_bytes / (ms_per_step / 1e3) / 1e9
+
+    kernels = {
+        "dispatch_bf16_kernel" if not wl.fp8 else "dispatch_fp8_kernel":
+            (dispatch_ms, nb["dispatch_kernel"], "ep_dispatch.hip"),
+        "combine_kernel": (combine_ms, nb["combine_kernel"], "ep_combine.hip"),
+    }
+    dom = max(kernels, key=lambda n: kernels[n][0])
+    dom_ms, dom_bytes, dom_src = kernels[dom]
+    achieved = dom_bytes / (dom_ms / 1e3) / 1e9
+    traffic = read_traffic(dom, dom_src, wl.name)
+
+    copy_gbps = measure_copy_gbps(torch)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3" if wl.fp8 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": wl.T, "hidden": wl.H, "experts": wl.E,
+                   "topk": wl.k, "capacity": wl.cap,
+                   "payload": "e4m3" if wl.fp8 else "bf16", "seed": wl.seed,
+                   "routing": {1: "uniform distinct", 2: "uniform distinct",
+                               3: "group-limited 8x32 top-4 groups",
+                               4: "Zipf 1.2 without replacement",
+                               5: "group-limited + 16 hot experts at 1.5x"}[wl.cid],
+                   "parallelism": "single GPU, all experts local"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": dom_bytes,
+                     "avg_launch_us": round(dom_ms * 1e3, 3)},
+        "detail": {
+            "us_per_call": {"layout": round(layout_ms * 1e3, 3),
+                            "dispatch": round(dispatch_ms * 1e3, 3),
+                            "dispatch_incl_layout": round((layout_ms + dispatch_ms) * 1e3, 3),
+                            "combine": round(combine_ms * 1e3, 3)},
+            "GBps": {"dispatch_incl_layout": round(nb["dispatch_total"] / ((layout_ms + dispatch_ms) / 1e3) / 1e9, 2),
+                     "dispatch_kernel": round(nb["dispatch_kernel"] / (dispatch_ms / 1e3) / 1e9, 2),
+                     "combine_kernel": round(nb["combine_kernel"] / (combine_ms / 1e3) / 1e9, 2)},
+            "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+            "algorithmic_bytes": nb,
+            "device_copy_GBps_1GiB": round(copy_gbps, 1),
+            "device": torch.cuda.get_device_name(0),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, eo_host, total_bytes, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,69 @@
+// ep_device.h -- device-side helpers shared by the libep kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ep {
+
+constexpr int kWave = 64;
+
+// Lanes below this one in the wave.
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    return (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+}
+
+__device__ __forceinline__ uint32_t lane_id() {
+    return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// Lanes of `active` whose `key` equals this lane's key, found with one ballot
+// per key bit (keys < 2^nbits).  Every lane of the wave must execute it.
+__device__ __forceinline__ uint64_t match_peers(uint32_t key, int nbits, uint64_t active) {
+    uint64_t m = active;
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (key >> b) & 1u;
+        const uint64_t bal = __ballot(bit);
+        m &= bit ? bal : ~bal;
+    }
+    return m;
+}
+
+// bf16 bit patterns (two per 32-bit word, low half first) -> fp32, exact.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN -> quiet NaN with its sign.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// fp32 -> OCP E4M3FN code, round to nearest even, saturating to +-448, sign
+// kept on zero.  Input must not be NaN.
+//   |v| >= 448            -> 0x7E (everything from 448 up rounds to 448 once
+//                            the format's top code is NaN and values saturate)
+//   2^-6 <= |v| < 448     -> normal codes: drop 20 of the 23 fraction bits with
+//                            round-half-even on the integer pattern, then move
+//                            the exponent bias from 127 to 7
+//   |v| < 2^-6            -> subnormal codes m * 2^-9: round |v| * 2^9 to the
+//                            nearest even integer (m = 8 is exactly 2^-6 = 0x08)
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    uint32_t code;
+    if (a >= 0x43e00000u) {
+        code = 0x7eu;
+    } else if (a >= 0x3c800000u) {
+        const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+        code = (r >> 20) - (120u << 3);
+    } else {
+        code = static_cast<uint32_t>(__builtin_rintf(__uint_as_float(a) * 512.0f));
+    }
+    return sign | code;
+}
+
+}  // namespace ep

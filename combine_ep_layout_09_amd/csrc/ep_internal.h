@@ -1,0 +1,34 @@
+// ep_internal.h -- launch helpers behind the libep C ABI (not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ep.h"
+
+namespace ep {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopk = 32;
+constexpr int kMaxHidden = 65536;
+constexpr int kLayoutThreads = 256;
+
+// Partition of the T*k routing entries into layout blocks.
+struct LayoutGeometry {
+    int64_t entries;   // T*k
+    int32_t chunk;     // entries per block, a multiple of kLayoutThreads
+    int32_t blocks;    // >= 1
+};
+
+LayoutGeometry layout_geometry(const ep_problem& p);
+int64_t layout_workspace_bytes(const ep_problem& p);
+
+hipError_t launch_layout(const ep_problem& p, const int32_t* topk_idx, const ep_layout_t& out,
+                         int32_t* block_hist, hipStream_t stream);
+hipError_t launch_dispatch(const ep_problem& p, const void* x, const int32_t* slot_of,
+                           void* recv_x, float* recv_scales, hipStream_t stream);
+hipError_t launch_combine(const ep_problem& p, const void* expert_out, const int32_t* slot_of,
+                          const float* topk_weights, void* y, hipStream_t stream);
+hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);
+
+}  // namespace ep

@@ -1,0 +1,310 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle.
+
+Bar: layout arrays, dispatch payload bytes and scale bits are bit-exact;
+combine output equals the oracle's bf16 bit for bit or lies within 2^-8
+relative of the oracle's fp32 sum (one bf16 ulp); the bit-exact fraction is
+reported.  Receive buffers are pre-filled with 0xFF bytes (NaN in bf16 and in
+E4M3FN) so that rows the method must not write are checked untouched, and
+expert-output rows no entry uses are NaN so that reading them would show.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import combine_ep_layout_09_amd as ep
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+NAN_BF16 = 0x7FC0
+
+
+def dev_bf16(u16):
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def host_u16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class Case:
+    def __init__(self, T, H, k, E, cap, fp8, x, idx, w, eo, name="case"):
+        self.T, self.H, self.k, self.E, self.cap, self.fp8 = T, H, k, E, cap, bool(fp8)
+        self.x, self.idx, self.w, self.eo, self.name = x, idx, w, eo, name
+
+    @property
+    def R(self):
+        return self.T * self.k if self.cap == 0 else self.E * self.cap
+
+    @classmethod
+    def from_workload(cls, wl, nan_unused=True):
+        eo = wl.expert_out()
+        c = cls(wl.T, wl.H, wl.k, wl.E, wl.cap, wl.fp8, wl.x, wl.topk_idx, wl.topk_weights, eo,
+                name=wl.name)
+        if nan_unused:
+            c.nan_unused_rows()
+        return c
+
+    def nan_unused_rows(self):
+        ref = oracle.layout(self.idx, self.E, self.cap)
+        self.eo = self.eo.copy()
+        self.eo[ref["src_of_slot"] < 0] = NAN_BF16
+
+
+def run_gpu(c, stream=None):
+    prob = ep.Problem(c.T, c.H, c.k, c.E, c.cap, c.fp8)
+    print(f"[gpu] {c.name}: {prob!r}", flush=True)
+    lay = ep.Layout.empty(prob, DEV)
+    for t in (lay.count, lay.offset, lay.slot_of, lay.src_of_slot, lay.status):
+        t.fill_(-7)
+    ws = ep.alloc_workspace(prob, DEV)
+    ws.fill_(0xAB)
+    recv_x, recv_s = ep.alloc_recv(prob, DEV)
+    recv_x.view(torch.uint8).fill_(0xFF)
+    if recv_s is not None:
+        recv_s.view(torch.uint8).fill_(0xFF)
+    y = torch.empty((c.T, c.H), dtype=torch.bfloat16, device=DEV)
+    y.view(torch.int16).fill_(0x5555)
+    idx = torch.from_numpy(np.ascontiguousarray(c.idx, np.int32)).to(DEV)
+    w = torch.from_numpy(np.ascontiguousarray(c.w, np.float32)).to(DEV)
+    x = dev_bf16(c.x)
+    eo = dev_bf16(c.eo)
+    torch.cuda.synchronize()
+    ctx = torch.cuda.stream(stream) if stream is not None else torch.cuda.stream(torch.cuda.current_stream())
+    with ctx:
+        ep.ep_layout(prob, idx, lay, ws)
+        ep.ep_dispatch(prob, x, lay, recv_x, recv_s)
+        ep.ep_combine(prob, eo, lay, w, y)
+    torch.cuda.synchronize()
+    out = {n: getattr(lay, n).cpu().numpy() for n in ("count", "offset", "slot_of", "src_of_slot", "status")}
+    out["recv_x"] = recv_x.view(torch.uint8).cpu().numpy().reshape(c.R, c.H * (1 if c.fp8 else 2))
+    out["recv_s"] = None if recv_s is None else recv_s.cpu().numpy()
+    out["y"] = host_u16(y)
+    return out
+
+
+def check_case(c, got, tokens=None):
+    """Compare one run with the oracle.  tokens: None = every token, else the
+    token ids whose receive rows and combine outputs are checked."""
+    ref = oracle.layout(c.idx, c.E, c.cap)
+    for n in ("count", "offset", "slot_of", "src_of_slot", "status"):
+        np.testing.assert_array_equal(got[n], ref[n], err_msg=f"{c.name}: layout {n}")
+    H = c.H
+    pb = 1 if c.fp8 else 2
+    placed = ref["src_of_slot"] >= 0
+    # rows no entry fills keep the 0xFF sentinel (payload and scales)
+    assert (got["recv_x"][~placed] == 0xFF).all(), f"{c.name}: unused receive rows written"
+    if c.fp8:
+        assert (got["recv_s"][~placed].view(np.uint32) == 0xFFFFFFFF).all()
+    if c.T == 0:
+        return 1.0
+    tok = np.arange(c.T) if tokens is None else np.asarray(tokens)
+    s_sel = ref["slot_of"][tok]                       # [n, k] global receive rows
+    rows = s_sel[s_sel >= 0]                          # in (t, j) order
+    compact = np.full_like(s_sel, -1)
+    compact[s_sel >= 0] = np.arange(len(rows), dtype=np.int32)
+    x_sel = np.ascontiguousarray(c.x[tok])
+    if c.fp8:
+        rx, rs = oracle.dispatch(x_sel, compact, len(rows), True)
+    else:
+        rx, _ = oracle.dispatch(x_sel, compact, len(rows), False)
+        rx = rx.view(np.uint8)
+    np.testing.assert_array_equal(got["recv_x"][rows], rx, err_msg=f"{c.name}: payload")
+    if c.fp8:
+        np.testing.assert_array_equal(got["recv_s"][rows].view(np.uint32), rs.view(np.uint32),
+                                      err_msg=f"{c.name}: scales")
+    ry, racc = oracle.combine(c.eo, s_sel, np.ascontiguousarray(c.w[tok]))
+    gy = got["y"][tok]
+    gyf = oracle.bf16_to_float(gy).astype(np.float64)
+    racc = racc.astype(np.float64)
+    exact = gy == ry
+    ok = exact | (np.abs(gyf - racc) <= 2.0 ** -8 * np.abs(racc))
+    assert ok.all(), f"{c.name}: combine outside tolerance at {np.argwhere(~ok)[:5]}"
+    frac = float(exact.mean())
+    print(f"[gpu] {c.name}: layout+dispatch bit-exact, combine bit-exact fraction {frac:.6f} "
+          f"({int(exact.sum())}/{exact.size})", flush=True)
+    return frac
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+def test_workload_full(cid):
+    c = Case.from_workload(workloads.make(cid))
+    check_case(c, run_gpu(c))
+
+
+def test_workload_large_prefill_sampled():
+    """T=16384, H=7168, E=256, k=8, FP8: full layout check; payload, scales and
+    combine checked on sampled tokens (first, last, a ragged spread)."""
+    c = Case.from_workload(workloads.make(5), nan_unused=False)
+    got = run_gpu(c)
+    rng = np.random.default_rng(0)
+    tokens = np.unique(np.concatenate([[0, 1, c.T - 1], rng.choice(c.T, 509, replace=False)]))
+    check_case(c, got, tokens)
+    # properties that hold for every row at any size
+    assert got["status"].tolist() == [0, 0]
+    assert (got["recv_x"][:, :] != 0xFF).any(axis=1).all()
+    assert np.isfinite(got["recv_s"]).all() and (got["recv_s"] >= 0).all()
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+
+def _random_case(T, H, k, E, cap, fp8, seed, ids=None, name="edge", scale=1.0):
+    rng = np.random.default_rng(seed)
+    x = workloads.to_bf16_bits((rng.standard_normal((T, H)) * scale).astype(np.float32))
+    if ids is None:
+        ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    R = T * k if cap == 0 else E * cap
+    eo = workloads.to_bf16_bits(rng.standard_normal((R, H)).astype(np.float32))
+    c = Case(T, H, k, E, cap, fp8, x, np.asarray(ids, np.int32).reshape(T, k), w, eo, name=name)
+    c.nan_unused_rows()
+    return c
+
+
+EDGE = [
+    dict(T=0, H=256, k=2, E=8, cap=0, fp8=False, name="empty_T0"),
+    dict(T=0, H=256, k=2, E=8, cap=4, fp8=True, name="empty_T0_capacity"),
+    dict(T=1, H=128, k=1, E=1, cap=0, fp8=True, name="single_token_single_expert_H128"),
+    dict(T=1, H=8, k=3, E=5, cap=0, fp8=False, name="smallest_hidden_H8"),
+    dict(T=37, H=136, k=3, E=5, cap=0, fp8=False, name="ragged_hidden_H136"),
+    dict(T=1000, H=264, k=7, E=33, cap=0, fp8=False, name="multi_block_ragged_tail"),
+    dict(T=3001, H=128, k=5, E=1024, cap=0, fp8=True, name="max_experts"),
+    dict(T=129, H=256, k=32, E=64, cap=0, fp8=False, name="max_topk"),
+    dict(T=300, H=384, k=4, E=1, cap=0, fp8=True, name="one_expert"),
+    dict(T=2500, H=256, k=6, E=7, cap=3, fp8=True, name="capacity_overflow"),
+    dict(T=50, H=2304, k=4, E=16, cap=64, fp8=False, name="capacity_bf16_no_overflow"),
+]
+
+
+@pytest.mark.parametrize("spec", EDGE, ids=[e["name"] for e in EDGE])
+def test_edge_shapes(spec):
+    spec = dict(spec)
+    name = spec.pop("name")
+    c = _random_case(**spec, seed=zlib.crc32(name.encode()) % 1000, name=name)
+    check_case(c, run_gpu(c))
+
+
+def test_duplicate_and_invalid_ids():
+    rng = np.random.default_rng(9)
+    T, k, E = 700, 4, 12
+    ids = rng.integers(0, E, size=(T, k))
+    ids[::7, 1] = ids[::7, 0]                     # duplicates inside a row
+    ids[::11, 2] = -1                              # below range
+    ids[::13, 3] = E                               # one past the end
+    ids[::17, 0] = 1 << 30                         # far out of range
+    ids[5] = 3                                     # all k entries to one expert
+    for cap, fp8 in ((0, False), (0, True), (40, True)):
+        c = _random_case(T, 256, k, E, cap, fp8, seed=cap, ids=ids, name=f"dup_invalid_cap{cap}")
+        got = run_gpu(c)
+        check_case(c, got)
+        assert got["status"][0] == int(((ids < 0) | (ids >= E)).sum())
+
+
+def test_fp8_special_rows():
+    """All-zero rows and blocks (scale 0), blocks of bf16 subnormals only,
+    negative zeros and tiny negatives, huge/tiny mixes whose quotients
+    underflow, x100 outliers, and quotients next to E4M3 rounding midpoints."""
+    rng = np.random.default_rng(31)
+    T, H, E, k = 12, 1024, 4, 2
+    xf = rng.standard_normal((T, H)).astype(np.float32)
+    xf[0] = 0.0                                            # whole row zero
+    xf[1, 128:256] = 0.0                                   # one zero block
+    xf[1, 256:384] = -0.0                                  # negative-zero block
+    sub = (np.arange(1, 129, dtype=np.uint32) << 16).view(np.float32)
+    xf[2, :128] = sub * np.where(np.arange(128) % 2, -1, 1)  # bf16 subnormals only
+    xf[3, :128] = -(2.0 ** -40) * rng.random(128)            # tiny negatives
+    xf[3, 0] = -3.0e38                                       # dominated block: quotients underflow
+    xf[4] *= 100.0                                           # outlier row
+    tab = oracle.e4m3_decode_table()
+    pos = tab[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2
+    for b in range(H // 128):                                # block max 448 * 2^m, midpoints inside
+        m = int(rng.integers(-8, 8))
+        xf[5, 128 * b: 128 * b + 126] = rng.choice(mids, 126) * 2.0 ** m * rng.choice([-1, 1], 126)
+        xf[5, 128 * b + 126] = 448.0 * 2.0 ** m
+        xf[5, 128 * b + 127] = -(2.0 ** (m - 10))            # exact tie with zero
+    x = workloads.to_bf16_bits(xf)
+    ids = np.stack([np.arange(T) % E, (np.arange(T) + 1) % E], axis=1).astype(np.int32)
+    w = np.full((T, k), 0.5, np.float32)
+    eo = workloads.to_bf16_bits(rng.standard_normal((T * k, H)).astype(np.float32))
+    for cap in (0, 8):
+        c = Case(T, H, k, E, cap, True, x, ids, w, eo if cap == 0 else
+                 workloads.to_bf16_bits(rng.standard_normal((E * cap, H)).astype(np.float32)),
+                 name=f"fp8_special_cap{cap}")
+        c.nan_unused_rows()
+        check_case(c, run_gpu(c))
+
+
+def test_non_default_stream():
+    c = _random_case(333, 512, 4, 16, 0, True, seed=5, name="side_stream")
+    s = torch.cuda.Stream()
+    check_case(c, run_gpu(c, stream=s))
+
+
+def test_deterministic_reruns():
+    c = Case.from_workload(workloads.make(3))
+    a = run_gpu(c)
+    b = run_gpu(c)
+    for n in a:
+        if a[n] is not None:
+            assert np.array_equal(a[n], b[n]), n
+
+
+def test_identity_round_trip():
+    """dispatch (bf16) -> identity experts -> combine with weights summing to 1
+    returns x bit for bit, on the GPU alone."""
+    wl = workloads.make(3, T=512)
+    prob = ep.Problem(wl.T, wl.H, wl.k, wl.E, 0, 0)
+    lay = ep.Layout.empty(prob, DEV)
+    ws = ep.alloc_workspace(prob, DEV)
+    recv_x, _ = ep.alloc_recv(prob, DEV)
+    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=DEV)
+    idx = torch.from_numpy(wl.topk_idx).to(DEV)
+    w = torch.from_numpy(wl.topk_weights).to(DEV)
+    x = dev_bf16(wl.x)
+    ep.ep_layout(prob, idx, lay, ws)
+    ep.ep_dispatch(prob, x, lay, recv_x)
+    ep.ep_combine(prob, recv_x, lay, w, y)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_u16(y), wl.x)
+
+
+# ---------------------------------------------------------------------------
+# the E4M3FN encoder, every binary32 input
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("sign", [0, 0x80000000], ids=["positive", "negative"])
+def test_e4m3_encoder_exhaustive(sign):
+    """Every finite binary32: the device encoder equals torch's CPU
+    float8_e4m3fn conversion where that conversion is defined to round
+    (|v| <= 464; torch == oracle there, pinned on the CPU), and 0x7E / 0xFE
+    (saturation) above; plus the oracle itself on a strided subset."""
+    chunk = 1 << 27
+    lim464 = int(np.array(464.0, np.float32).view(np.uint32))
+    inf = 0x7F800000
+    out = torch.empty(chunk, dtype=torch.uint8, device=DEV)
+    if True:
+        for lo in range(0, inf, chunk):
+            hi = min(inf, lo + chunk)
+            bits = (np.arange(lo, hi, dtype=np.uint64).astype(np.uint32) | np.uint32(sign))
+            v = bits.view(np.float32)
+            vin = torch.from_numpy(v).to(DEV)
+            ep.ep_e4m3_encode(vin, out[: hi - lo])
+            got = out[: hi - lo].cpu().numpy()
+            mag = bits & 0x7FFFFFFF
+            inr = mag <= lim464
+            want = torch.from_numpy(v[inr]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(got[inr], want), hex(lo | sign)
+            assert (got[~inr] == (0xFE if sign else 0x7E)).all(), hex(lo | sign)
+            sub = slice(0, hi - lo, 4099)
+            assert np.array_equal(got[sub], oracle.e4m3_encode(v[sub])), hex(lo | sign)
