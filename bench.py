@@ -21,7 +21,6 @@ on the same inputs (serial, one core).
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -77,6 +76,41 @@ def read_traffic(kernel, source, workload):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+class HipEvents:
+    """Timing events recorded on the stream the kernels run on, created with
+    hipEventDisableSystemFence: recording one does not write back and
+    invalidate the caches, so the kernels between two events run as they
+    would without the events."""
+
+    _FLAGS = 0x20000000  # hipEventDisableSystemFence (timing stays enabled)
+
+    def __init__(self, n):
+        import ctypes
+        self._ct = ctypes
+        self.lib = ctypes.CDLL("libamdhip64.so.7")  # the runtime torch already loaded
+        self.ev = []
+        for _ in range(n):
+            h = ctypes.c_void_p()
+            if self.lib.hipEventCreateWithFlags(ctypes.byref(h), ctypes.c_uint(self._FLAGS)) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(h)
+
+    def record(self, i, stream_handle):
+        if self.lib.hipEventRecord(self.ev[i], self._ct.c_void_p(stream_handle)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        ms = self._ct.c_float()
+        if self.lib.hipEventElapsedTime(self._ct.byref(ms), self.ev[a], self.ev[b]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for h in self.ev:
+            self.lib.hipEventDestroy(h)
+        self.ev = []
 
 
 def measure_copy_gbps(torch, nbytes=1 << 30, reps=10):
@@ -173,23 +207,32 @@ def main():
     nb = algorithmic_bytes(wl, count)
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    sh = stream.cuda_stream
+    ev = HipEvents(4 * K)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        ev[i][0].record(stream)
+        ev.record(4 * i, sh)
         do_layout(stream)
-        ev[i][1].record(stream)
+        ev.record(4 * i + 1, sh)
         do_dispatch(stream)
-        ev[i][2].record(stream)
+        ev.record(4 * i + 2, sh)
         do_combine(stream)
-        ev[i][3].record(stream)
+        ev.record(4 * i + 3, sh)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     print(f"[bench] timed {K} steps in {wall:.4f} s", file=sys.stderr, flush=True)
 
     def mean_ms(a, b):
-        return sum(ev[i][a].elapsed_time(ev[i][b]) for i in range(K)) / K
+        return sum(ev.elapsed_ms(4 * i + a, 4 * i + b) for i in range(K)) / K
+
+    # The same steps with no events between kernels, for comparison only.
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(K):
+        step()
+    torch.cuda.synchronize()
+    wall_no_events = time.perf_counter() - t1
 
     layout_ms, dispatch_ms, combine_ms = mean_ms(0, 1), mean_ms(1, 2), mean_ms(2, 3)
     ms_per_step = wall / K * 1e3
@@ -243,6 +286,7 @@ def main():
                      "dispatch_kernel": round(nb["dispatch_kernel"] / (dispatch_ms / 1e3) / 1e9, 2),
                      "combine_kernel": round(nb["combine_kernel"] / (combine_ms / 1e3) / 1e9, 2)},
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+            "ms_per_step_without_kernel_events": round(wall_no_events / K * 1e3, 5),
             "algorithmic_bytes": nb,
             "device_copy_GBps_1GiB": round(copy_gbps, 1),
             "device": torch.cuda.get_device_name(0),
@@ -253,6 +297,7 @@ def main():
         out["cpu_baseline"] = cpu_baseline(wl, eo_host, total_bytes, args.cpu_seconds)
     else:
         out["cpu_baseline"] = None
+    ev.close()
     print(json.dumps(out), flush=True)
     return 0
 

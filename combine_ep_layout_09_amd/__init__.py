@@ -77,6 +77,9 @@ def load_library():
     if not os.path.exists(_LIB_PATH):
         from . import build as _build
         _build.build()
+    # torch ships its own HIP runtime under the same soname; loading it first
+    # makes libep bind to that runtime, so torch's streams and memory are ours.
+    _torch()
     lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.POINTER(Problem)
     L = ctypes.POINTER(_LayoutPtrs)

@@ -11,10 +11,14 @@
 // holds).  Every lane follows exactly that chain for each of its channels, so
 // the result does not depend on the launch shape.
 //
-// One workgroup per token.  The slots and weights of the token are uniform
-// (scalar loads).  For each 16-byte piece of the output row a lane first
-// issues the loads of up to 8 expert rows, then runs the FMA chain, so up to
-// 8 independent 16-byte loads per lane are in flight.
+// Launch shape: one workgroup per (token, column tile), VPL 16-byte pieces
+// per lane spaced one workgroup-width apart (the same tiling as dispatch).
+// Entries are taken in batches of KB: the lane first issues the loads of all
+// KB expert rows for all its pieces -- with no branches, so they are all in
+// flight together -- and then runs the FMA chain.  An entry without a slot
+// loads a row the token does use (a cache hit) and its FMA result is
+// discarded by a select, which keeps the chain exactly "skip this term".
+// Expert rows are read with non-temporal loads: each is read once.
 
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -22,54 +26,93 @@
 namespace ep {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBatch = 8;   // expert rows loaded before their FMAs
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ void fma8(float (&acc)[8], float w, const uint4& p) {
-    acc[0] = __builtin_fmaf(w, bf16_lo(p.x), acc[0]);
-    acc[1] = __builtin_fmaf(w, bf16_hi(p.x), acc[1]);
-    acc[2] = __builtin_fmaf(w, bf16_lo(p.y), acc[2]);
-    acc[3] = __builtin_fmaf(w, bf16_hi(p.y), acc[3]);
-    acc[4] = __builtin_fmaf(w, bf16_lo(p.z), acc[4]);
-    acc[5] = __builtin_fmaf(w, bf16_hi(p.z), acc[5]);
-    acc[6] = __builtin_fmaf(w, bf16_lo(p.w), acc[6]);
-    acc[7] = __builtin_fmaf(w, bf16_hi(p.w), acc[7]);
-}
+constexpr int kMaxThreads = 1024;
 
-__global__ __launch_bounds__(kThreads) void combine_kernel(
-        const uint4* __restrict__ eo, int nvec, int k, const int32_t* __restrict__ slot_of,
-        int64_t R, const float* __restrict__ weights, uint4* __restrict__ y) {
+__device__ __forceinline__ float lo16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <int KB, int VPL>
+__global__ __launch_bounds__(kMaxThreads) void combine_kernel(
+        const u32x4* __restrict__ eo, int nvec, int k, const int32_t* __restrict__ slot_of,
+        int64_t R, const float* __restrict__ weights, u32x4* __restrict__ y) {
     const int t = blockIdx.x;
     const int32_t* slots = slot_of + static_cast<int64_t>(t) * k;
     const float* w = weights + static_cast<int64_t>(t) * k;
-    uint4* out = y + static_cast<int64_t>(t) * nvec;
-    for (int v = threadIdx.x; v < nvec; v += kThreads) {
-        float acc[8];
+    const int base = blockIdx.y * blockDim.x * VPL + threadIdx.x;
+    int v[VPL];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
-        for (int j0 = 0; j0 < k; j0 += kBatch) {
-            uint4 buf[kBatch];
+    for (int u = 0; u < VPL; ++u) v[u] = min(base + u * static_cast<int>(blockDim.x), nvec - 1);
+
+    // A receive row this token uses, for the loads of entries it does not use.
+    int32_t safe = -1;
+    for (int j = 0; j < k; ++j) {
+        const int32_t s = slots[j];
+        if (s >= 0 && s < R) {
+            safe = s;
+            break;
+        }
+    }
+
+    float acc[VPL][8];
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int j = j0 + u;
-                if (j < k) {
-                    const int32_t slot = slots[j];
-                    if (slot >= 0 && slot < R) buf[u] = eo[static_cast<int64_t>(slot) * nvec + v];
+    for (int u = 0; u < VPL; ++u)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[u][c] = 0.0f;
+
+    if (safe >= 0) {
+        for (int j0 = 0; j0 < k; j0 += KB) {
+            bool ok[KB];
+            float wj[KB];
+            const u32x4* src[KB];
+#pragma unroll
+            for (int jj = 0; jj < KB; ++jj) {
+                const int j = j0 + jj;
+                const int32_t s = (j < k) ? slots[j] : -1;
+                ok[jj] = s >= 0 && s < R;
+                wj[jj] = ok[jj] ? w[j] : 0.0f;
+                src[jj] = eo + static_cast<int64_t>(ok[jj] ? s : safe) * nvec;
+            }
+            u32x4 buf[VPL][KB];
+#pragma unroll
+            for (int jj = 0; jj < KB; ++jj)
+#pragma unroll
+                for (int u = 0; u < VPL; ++u) buf[u][jj] = __builtin_nontemporal_load(src[jj] + v[u]);
+#pragma unroll
+            for (int jj = 0; jj < KB; ++jj) {
+#pragma unroll
+                for (int u = 0; u < VPL; ++u) {
+                    const u32x4 p = buf[u][jj];
+                    const float f[8] = {lo16(p.x), hi16(p.x), lo16(p.y), hi16(p.y),
+                                        lo16(p.z), hi16(p.z), lo16(p.w), hi16(p.w)};
+#pragma unroll
+                    for (int c = 0; c < 8; ++c) {
+                        const float a = __builtin_fmaf(wj[jj], f[c], acc[u][c]);
+                        acc[u][c] = ok[jj] ? a : acc[u][c];
+                    }
                 }
             }
-#pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int j = j0 + u;
-                if (j < k && slots[j] >= 0 && slots[j] < R) fma8(acc, w[j], buf[u]);
-            }
         }
-        uint4 r;
-        r.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
-        r.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
-        r.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
-        r.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
-        out[v] = r;
     }
+
+    u32x4* out = y + static_cast<int64_t>(t) * nvec;
+#pragma unroll
+    for (int u = 0; u < VPL; ++u) {
+        u32x4 r;
+        r.x = f32_to_bf16_rne(acc[u][0]) | (f32_to_bf16_rne(acc[u][1]) << 16);
+        r.y = f32_to_bf16_rne(acc[u][2]) | (f32_to_bf16_rne(acc[u][3]) << 16);
+        r.z = f32_to_bf16_rne(acc[u][4]) | (f32_to_bf16_rne(acc[u][5]) << 16);
+        r.w = f32_to_bf16_rne(acc[u][6]) | (f32_to_bf16_rne(acc[u][7]) << 16);
+        out[v[u]] = r;
+    }
+}
+
+template <int KB>
+void launch_kb(dim3 grid, int threads, hipStream_t stream, const u32x4* eo, int nvec, int k,
+               const int32_t* slot_of, int64_t R, const float* w, u32x4* y) {
+    hipLaunchKernelGGL((combine_kernel<KB, 2>), grid, dim3(threads), 0, stream, eo, nvec, k,
+                       slot_of, R, w, y);
 }
 
 }  // namespace
@@ -80,9 +123,22 @@ hipError_t launch_combine(const ep_problem& p, const void* expert_out, const int
     if (T == 0) return hipSuccess;
     const int64_t R = p.capacity == 0 ? static_cast<int64_t>(T) * p.num_topk
                                       : static_cast<int64_t>(p.num_experts) * p.capacity;
-    hipLaunchKernelGGL(combine_kernel, dim3(T), dim3(kThreads), 0, stream,
-                       static_cast<const uint4*>(expert_out), p.hidden / 8, p.num_topk, slot_of,
-                       R, topk_weights, static_cast<uint4*>(y));
+    const int nvec = p.hidden / 8;
+    const TileShape s = row_tile_shape(nvec, 2);
+    const dim3 grid(T, s.tiles);
+    const auto* eo = static_cast<const u32x4*>(expert_out);
+    auto* yo = static_cast<u32x4*>(y);
+    const int k = p.num_topk;
+    switch (k) {
+        case 1: launch_kb<1>(grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
+        case 2: launch_kb<2>(grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
+        case 3: launch_kb<3>(grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
+        case 4: launch_kb<4>(grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
+        case 5: launch_kb<5>(grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
+        case 6: launch_kb<6>(grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
+        case 7: launch_kb<7>(grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
+        default: launch_kb<8>(grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
+    }
     return hipGetLastError();
 }
 

@@ -7,17 +7,26 @@
 // triple-buffered prefetch", Summary; on one GPU the message is written
 // straight into the expert-major receive rows chosen by the layout.
 //
-// One workgroup per token.  The token's k slots are uniform across the
-// workgroup (scalar loads).  A slot of -1 (or one outside [0, R), which a
-// layout of this problem never holds) writes nothing.  Each lane loads 16-byte pieces of the token row
-// once, holds them in registers, and stores them to every slot, so x is read
-// from HBM exactly once however large k is.
+// Launch shape: one workgroup per (token, column tile).  A lane owns VPL
+// 16-byte pieces of the row, spaced one workgroup-width apart so that every
+// load and store instruction of a wave covers 1 KiB of contiguous memory.
+// The host picks the workgroup width so that a tile covers the row with as
+// little slack as possible; lanes past the end of the row redo the last piece
+// (last 16-lane group for FP8) and store the same bytes to the same place,
+// which keeps the loads free of branches.  All VPL loads are issued before
+// any store, the row is read from HBM once however large k is, and the
+// token's k slots are uniform across the workgroup (scalar loads).  Receive
+// rows are written with non-temporal stores: they are not read again by this
+// kernel and should not evict other data from the caches.
+//
+// A slot of -1 (or one outside [0, R), which a layout of this problem never
+// holds) writes nothing.
 //
 // FP8: a lane holds 8 channels, so a 128-channel block is 16 adjacent lanes
 // (one DPP row).  The block maximum of |x| is reduced across the row, the
 // scale is amax / 448 (IEEE fp32 division), each channel is divided by it
 // (IEEE fp32 division) and encoded with round-to-nearest-even.  The block
-// scales of the token are collected in LDS and written as one contiguous run
+// scales of the tile are collected in LDS and written as one contiguous run
 // per slot.
 
 #include "ep_device.h"
@@ -26,32 +35,32 @@
 namespace ep {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kUnroll = 4;   // 16-byte pieces in flight per lane
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-__global__ __launch_bounds__(kThreads) void dispatch_bf16_kernel(
-        const uint4* __restrict__ x, int nvec, int k, const int32_t* __restrict__ slot_of,
-        int64_t R, uint4* __restrict__ recv) {
+constexpr int kMaxThreads = 1024;
+
+template <int VPL>
+__global__ __launch_bounds__(kMaxThreads) void dispatch_bf16_kernel(
+        const u32x4* __restrict__ x, int nvec, int k, const int32_t* __restrict__ slot_of,
+        int64_t R, u32x4* __restrict__ recv) {
     const int t = blockIdx.x;
     const int32_t* slots = slot_of + static_cast<int64_t>(t) * k;
-    const uint4* row = x + static_cast<int64_t>(t) * nvec;
-    for (int v0 = threadIdx.x; v0 < nvec; v0 += kThreads * kUnroll) {
-        uint4 buf[kUnroll];
+    const u32x4* row = x + static_cast<int64_t>(t) * nvec;
+    const int base = blockIdx.y * blockDim.x * VPL + threadIdx.x;
+    int v[VPL];
+    u32x4 buf[VPL];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int v = v0 + u * kThreads;
-            if (v < nvec) buf[u] = row[v];
-        }
-        for (int j = 0; j < k; ++j) {
-            const int32_t slot = slots[j];
-            if (slot < 0 || slot >= R) continue;  // -1: no row; >= R: not this problem's
-            uint4* dst = recv + static_cast<int64_t>(slot) * nvec;
+    for (int u = 0; u < VPL; ++u) {
+        v[u] = min(base + u * static_cast<int>(blockDim.x), nvec - 1);
+        buf[u] = row[v[u]];
+    }
+    for (int j = 0; j < k; ++j) {
+        const int32_t slot = slots[j];
+        if (slot < 0 || slot >= R) continue;
+        u32x4* dst = recv + static_cast<int64_t>(slot) * nvec;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int v = v0 + u * kThreads;
-                if (v < nvec) dst[v] = buf[u];
-            }
-        }
+        for (int u = 0; u < VPL; ++u) __builtin_nontemporal_store(buf[u], dst + v[u]);
     }
 }
 
@@ -75,7 +84,7 @@ __device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, float scale
     return packed;
 }
 
-__device__ __forceinline__ float absmax8(const uint4& p) {
+__device__ __forceinline__ float absmax8(const u32x4& p) {
     float m = fabsf(bf16_lo(p.x));
     m = fmaxf(m, fabsf(bf16_hi(p.x)));
     m = fmaxf(m, fabsf(bf16_lo(p.y)));
@@ -87,69 +96,75 @@ __device__ __forceinline__ float absmax8(const uint4& p) {
     return m;
 }
 
-// nvec = H / 8 (multiple of 16); nblk = H / 128.
-__global__ __launch_bounds__(kThreads) void dispatch_fp8_kernel(
-        const uint4* __restrict__ x, int nvec, int nblk, int k,
-        const int32_t* __restrict__ slot_of, int64_t R, uint2* __restrict__ recv_q,
+// nvec = H / 8 (a multiple of 16); nblk = H / 128.  The workgroup width is a
+// multiple of 64, so 16-lane groups never straddle the end of the row: a group
+// past the end maps as a whole onto the row's last group.
+template <int VPL>
+__global__ __launch_bounds__(kMaxThreads) void dispatch_fp8_kernel(
+        const u32x4* __restrict__ x, int nvec, int nblk, int k,
+        const int32_t* __restrict__ slot_of, int64_t R, u32x2* __restrict__ recv_q,
         float* __restrict__ recv_scales) {
-    extern __shared__ float s_scale[];  // [nblk]
+    extern __shared__ float s_scale[];  // [blockDim * VPL / 16] scales of this tile
     const int t = blockIdx.x;
     const int32_t* slots = slot_of + static_cast<int64_t>(t) * k;
-    const uint4* row = x + static_cast<int64_t>(t) * nvec;
-    // Lanes of one 16-lane row are all in range or all out of range because
-    // nvec is a multiple of 16 and the loop start is a multiple of 64.
-    for (int v0 = 0; v0 < nvec; v0 += kThreads * kUnroll) {
-        uint4 buf[kUnroll];
+    const u32x4* row = x + static_cast<int64_t>(t) * nvec;
+    const int tile0 = blockIdx.y * blockDim.x * VPL;
+    int v[VPL];
+    u32x4 buf[VPL];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int v = v0 + u * kThreads + threadIdx.x;
-            if (v < nvec) buf[u] = row[v];
-        }
-        uint2 q[kUnroll];
+    for (int u = 0; u < VPL; ++u) {
+        const int vv = tile0 + u * static_cast<int>(blockDim.x) + threadIdx.x;
+        v[u] = (vv < nvec) ? vv : nvec - 16 + (vv & 15);
+        buf[u] = row[v[u]];
+    }
+    u32x2 q[VPL];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int v = v0 + u * kThreads + threadIdx.x;
-            if (v0 + u * kThreads < nvec) {  // uniform across the workgroup
-                const float amax = row16_max(v < nvec ? absmax8(buf[u]) : 0.0f);
-                const float scale = amax / 448.0f;
-                if (v < nvec) {
-                    q[u].x = quant4(buf[u].x, buf[u].y, scale);
-                    q[u].y = quant4(buf[u].z, buf[u].w, scale);
-                    if ((threadIdx.x & 15) == 0) s_scale[v >> 4] = scale;
-                }
-            }
-        }
-        for (int j = 0; j < k; ++j) {
-            const int32_t slot = slots[j];
-            if (slot < 0 || slot >= R) continue;  // -1: no row; >= R: not this problem's
-            uint2* dst = recv_q + static_cast<int64_t>(slot) * nvec;
+    for (int u = 0; u < VPL; ++u) {
+        const float amax = row16_max(absmax8(buf[u]));
+        const float scale = amax / 448.0f;
+        q[u].x = quant4(buf[u].x, buf[u].y, scale);
+        q[u].y = quant4(buf[u].z, buf[u].w, scale);
+        const int vv = tile0 + u * static_cast<int>(blockDim.x) + threadIdx.x;
+        if ((threadIdx.x & 15) == 0 && vv < nvec) s_scale[(vv - tile0) >> 4] = scale;
+    }
+    for (int j = 0; j < k; ++j) {
+        const int32_t slot = slots[j];
+        if (slot < 0 || slot >= R) continue;
+        u32x2* dst = recv_q + static_cast<int64_t>(slot) * nvec;
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int v = v0 + u * kThreads + threadIdx.x;
-                if (v < nvec) dst[v] = q[u];
-            }
-        }
+        for (int u = 0; u < VPL; ++u) __builtin_nontemporal_store(q[u], dst + v[u]);
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < k * nblk; i += kThreads) {
-        const int j = i / nblk;
-        const int blk = i - j * nblk;
+    // Scales: this tile covers blocks [tile0/16, tile0/16 + nb) of the row.
+    const int b0 = tile0 >> 4;
+    const int nb = min(static_cast<int>(blockDim.x) * VPL / 16, nblk - b0);
+    for (int i = threadIdx.x; i < k * nb; i += blockDim.x) {
+        const int j = i / nb;
+        const int b = i - j * nb;
         const int32_t slot = slots[j];
-        if (slot >= 0 && slot < R) recv_scales[static_cast<int64_t>(slot) * nblk + blk] = s_scale[blk];
+        if (slot >= 0 && slot < R)
+            recv_scales[static_cast<int64_t>(slot) * nblk + b0 + b] = s_scale[b];
     }
 }
 
 // Elementwise use of the same encoder, for callers that quantise other data.
-__global__ __launch_bounds__(kThreads) void e4m3_encode_kernel(
+__global__ __launch_bounds__(256) void e4m3_encode_kernel(
         const float* __restrict__ in, uint8_t* __restrict__ out, int64_t n) {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n;
          i += stride) {
         out[i] = static_cast<uint8_t>(f32_to_e4m3_rne(in[i]));
     }
 }
 
 }  // namespace
+
+TileShape row_tile_shape(int nvec, int vpl) {
+    const int lanes = (nvec + vpl - 1) / vpl;
+    const int tiles = (lanes + kMaxThreads - 1) / kMaxThreads;
+    const int per_tile = (lanes + tiles - 1) / tiles;
+    return {((per_tile + 63) / 64) * 64, tiles};
+}
 
 hipError_t launch_dispatch(const ep_problem& p, const void* x, const int32_t* slot_of,
                            void* recv_x, float* recv_scales, hipStream_t stream) {
@@ -158,26 +173,28 @@ hipError_t launch_dispatch(const ep_problem& p, const void* x, const int32_t* sl
     const int nvec = p.hidden / 8;
     const int64_t R = p.capacity == 0 ? static_cast<int64_t>(T) * p.num_topk
                                       : static_cast<int64_t>(p.num_experts) * p.capacity;
+    constexpr int kVpl = 2;
+    const TileShape s = row_tile_shape(nvec, kVpl);
+    const dim3 grid(T, s.tiles);
     if (p.use_fp8) {
-        const int nblk = p.hidden / 128;
-        hipLaunchKernelGGL(dispatch_fp8_kernel, dim3(T), dim3(kThreads),
-                           static_cast<size_t>(nblk) * 4, stream,
-                           static_cast<const uint4*>(x), nvec, nblk, p.num_topk, slot_of, R,
-                           static_cast<uint2*>(recv_x), recv_scales);
+        const size_t lds = static_cast<size_t>(s.threads) * kVpl / 16 * 4;
+        hipLaunchKernelGGL(dispatch_fp8_kernel<kVpl>, grid, dim3(s.threads), lds, stream,
+                           static_cast<const u32x4*>(x), nvec, p.hidden / 128, p.num_topk,
+                           slot_of, R, static_cast<u32x2*>(recv_x), recv_scales);
     } else {
-        hipLaunchKernelGGL(dispatch_bf16_kernel, dim3(T), dim3(kThreads), 0, stream,
-                           static_cast<const uint4*>(x), nvec, p.num_topk, slot_of, R,
-                           static_cast<uint4*>(recv_x));
+        hipLaunchKernelGGL(dispatch_bf16_kernel<kVpl>, grid, dim3(s.threads), 0, stream,
+                           static_cast<const u32x4*>(x), nvec, p.num_topk, slot_of, R,
+                           static_cast<u32x4*>(recv_x));
     }
     return hipGetLastError();
 }
 
 hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream) {
     if (n == 0) return hipSuccess;
-    int64_t blocks = (n + kThreads - 1) / kThreads;
+    int64_t blocks = (n + 255) / 256;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(e4m3_encode_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
-                       0, stream, in, out, n);
+    hipLaunchKernelGGL(e4m3_encode_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       stream, in, out, n);
     return hipGetLastError();
 }
 

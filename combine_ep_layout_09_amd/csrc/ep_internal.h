@@ -13,6 +13,14 @@ constexpr int kMaxTopk = 32;
 constexpr int kMaxHidden = 65536;
 constexpr int kLayoutThreads = 256;
 
+// Workgroup width (a multiple of 64, at most 1024) and number of column tiles
+// that cover a row of nvec 16-byte pieces with vpl pieces per lane.
+struct TileShape {
+    int threads;
+    int tiles;
+};
+TileShape row_tile_shape(int nvec, int vpl);
+
 // Partition of the T*k routing entries into layout blocks.
 struct LayoutGeometry {
     int64_t entries;   // T*k

@@ -95,10 +95,21 @@ __global__ __launch_bounds__(kThreads) void layout_rank_kernel(
     const int wave = tid / kWave;
     const uint32_t lane = lane_id();
 
-    // 1. Column sums of the block-histogram table.
+    // 1. Column sums of the block-histogram table, eight rows in flight.
     for (int e = tid; e <= E; e += kThreads) {
         int32_t tot = 0, pre = 0;
-        for (int bb = 0; bb < nblocks; ++bb) {
+        int bb = 0;
+        for (; bb + 8 <= nblocks; bb += 8) {
+            int32_t v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = block_hist[static_cast<int64_t>(bb + q) * (E + 1) + e];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                tot += v[q];
+                pre += (bb + q < b) ? v[q] : 0;
+            }
+        }
+        for (; bb < nblocks; ++bb) {
             const int32_t v = block_hist[static_cast<int64_t>(bb) * (E + 1) + e];
             tot += v;
             pre += (bb < b) ? v : 0;
@@ -225,12 +236,13 @@ __global__ __launch_bounds__(kThreads) void layout_rank_kernel(
 LayoutGeometry layout_geometry(const ep_problem& p) {
     LayoutGeometry g;
     g.entries = static_cast<int64_t>(p.num_tokens) * p.num_topk;
-    // Aim for at most ~64 blocks so that each block's column sums stay short,
-    // with 1..16 entries per thread.
-    int64_t per_thread = (g.entries + static_cast<int64_t>(kThreads) * 64 - 1) /
-                         (static_cast<int64_t>(kThreads) * 64);
+    // Aim for at most ~32 blocks so that each block's column sums stay short,
+    // with 1..64 entries per thread.
+    constexpr int64_t kTargetBlocks = 32;
+    int64_t per_thread = (g.entries + static_cast<int64_t>(kThreads) * kTargetBlocks - 1) /
+                         (static_cast<int64_t>(kThreads) * kTargetBlocks);
     if (per_thread < 1) per_thread = 1;
-    if (per_thread > 16) per_thread = 16;
+    if (per_thread > 64) per_thread = 64;
     g.chunk = static_cast<int32_t>(per_thread * kThreads);
     int64_t blocks = (g.entries + g.chunk - 1) / g.chunk;
     g.blocks = static_cast<int32_t>(blocks < 1 ? 1 : blocks);
