@@ -11,7 +11,6 @@ namespace ep {
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopk = 32;
 constexpr int kMaxHidden = 65536;
-constexpr int kLayoutThreads = 256;
 
 // Workgroup width (a multiple of 64, at most 1024) and number of column tiles
 // that cover a row of nvec 16-byte pieces with vpl pieces per lane.
@@ -24,8 +23,9 @@ TileShape row_tile_shape(int nvec, int vpl);
 // Partition of the T*k routing entries into layout blocks.
 struct LayoutGeometry {
     int64_t entries;   // T*k
-    int32_t chunk;     // entries per block, a multiple of kLayoutThreads
+    int32_t chunk;     // entries per block, a multiple of 256
     int32_t blocks;    // >= 1
+    bool single_pass;  // one kernel, no workspace traffic
 };
 
 LayoutGeometry layout_geometry(const ep_problem& p);

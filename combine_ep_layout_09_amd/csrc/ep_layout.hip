@@ -7,24 +7,28 @@
 // stable order inside an expert follows the order-consistency requirement in
 // "[GH-ISSUE #18] Reasons for not calling NVSHMEM public APIs?".
 //
-// Two kernels, both over the same partition of the T*k entries into blocks of
-// `chunk` consecutive entries (row-major (t, j) order):
+// The T*k entries (row-major (t, j) order) are split into blocks of `chunk`
+// consecutive entries; each workgroup ranks one block.  What a workgroup needs
+// before it can rank is, per expert, the number of valid entries in the whole
+// table (for the offsets) and in the blocks before its own (for the ranks).
 //
-//   layout_hist  each block builds its expert histogram in LDS (one LDS add
-//                per distinct expert per wave, found with key-bit ballots)
-//                and stores it, plus its count of invalid ids, as one row of
-//                the block-histogram table in the workspace.
-//   layout_rank  each block sums the table's columns (all blocks: totals;
-//                earlier blocks: its own prefix), scans the totals into
-//                offsets, then ranks its entries: per-wave histograms of its
-//                chunk give each wave a starting rank per expert, and inside
-//                a wave each 64-entry step ranks lanes against lower lanes with
-//                the same expert by ballot matching.  Block 0 writes count,
-//                offset and status; all blocks together mark empty receive
-//                rows with -1.
+// Single-pass path (tables up to kSinglePassMaxEntries entries, which covers
+// every decode and prefill batch in practice): one kernel.  Every workgroup
+// reads the whole routing table -- at most a few hundred KiB, served from L2
+// after the first touch -- and builds both histograms itself with LDS atomics.
+// No workgroup waits on another, so the kernel has no inter-block
+// synchronisation at all and costs one launch.
 //
-// The result is deterministic and does not depend on the order in which
-// blocks run: no block waits on another and no global atomics are used.
+// Two-pass path (larger tables): layout_hist writes each block's histogram to
+// the workspace, and layout_rank sums the table's columns.
+//
+// Both paths then run the same tail: wave 0 scans the totals into offsets;
+// workgroup 0 writes count, offset and status; the block's entries are split
+// into one contiguous run per ranking wave, per-wave histograms give each wave
+// its first rank per expert, and inside a wave each 64-entry step ranks a lane
+// against the lower lanes with the same expert, found with one ballot per key
+// bit.  All workgroups together mark empty receive rows with -1.  The result
+// is deterministic and independent of workgroup scheduling.
 
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -32,39 +36,18 @@
 namespace ep {
 namespace {
 
-constexpr int kThreads = kLayoutThreads;
-constexpr int kWaves = kThreads / kWave;
+constexpr int kRankWaves = 4;                 // waves that rank a block's entries
+constexpr int kRankThreads = kRankWaves * kWave;
+constexpr int kSingleThreads = 1024;          // single-pass workgroup
+constexpr int64_t kSinglePassMaxEntries = 1 << 18;
 
 __device__ __forceinline__ int key_bits(int E) {
     // number of bits needed for ids 0..E-1
     return (E <= 1) ? 0 : 32 - __clz(E - 1);
 }
 
-__global__ __launch_bounds__(kThreads) void layout_hist_kernel(
-        const int32_t* __restrict__ idx, int64_t n, int E, int chunk,
-        int32_t* __restrict__ block_hist) {
-    extern __shared__ int32_t hist[];  // [E + 1]; hist[E] counts invalid ids
-    const int b = blockIdx.x;
-    for (int e = threadIdx.x; e <= E; e += kThreads) hist[e] = 0;
-    __syncthreads();
-
-    const int nbits = key_bits(E);
-    const int64_t begin = static_cast<int64_t>(b) * chunk;
-    const int64_t end = (begin + chunk < n) ? begin + chunk : n;
-    for (int64_t base = begin; base < begin + chunk; base += kThreads) {
-        const int64_t i = base + threadIdx.x;
-        const bool in = i < end;
-        const int32_t key = in ? idx[i] : -1;
-        const bool valid = in && static_cast<uint32_t>(key) < static_cast<uint32_t>(E);
-        const uint64_t active = __ballot(valid);
-        const uint64_t peers = match_peers(valid ? key : 0, nbits, active);
-        if (valid && (peers & lanemask_lt()) == 0) atomicAdd(&hist[key], __popcll(peers));
-        const uint64_t invalid = __ballot(in && !valid);
-        if (lane_id() == 0 && invalid) atomicAdd(&hist[E], __popcll(invalid));
-    }
-    __syncthreads();
-    int32_t* row = block_hist + static_cast<int64_t>(b) * (E + 1);
-    for (int e = threadIdx.x; e <= E; e += kThreads) row[e] = hist[e];
+__device__ __forceinline__ bool valid_id(int32_t key, int E) {
+    return static_cast<uint32_t>(key) < static_cast<uint32_t>(E);
 }
 
 // Inclusive scan across the 64 lanes of a wave.
@@ -78,25 +61,234 @@ __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v) {
     return v;
 }
 
-__global__ __launch_bounds__(kThreads) void layout_rank_kernel(
-        const int32_t* __restrict__ idx, int64_t n, int E, int cap, int chunk, int nblocks,
-        int64_t R, const int32_t* __restrict__ block_hist, int32_t* __restrict__ count,
-        int32_t* __restrict__ offset, int32_t* __restrict__ slot_of,
-        int32_t* __restrict__ src_of_slot, int32_t* __restrict__ status) {
-    extern __shared__ int32_t sm[];
-    int32_t* total = sm;               // [E]    entries per expert, all blocks
-    int32_t* prior = total + E;        // [E]    entries per expert in blocks before this one
-    int32_t* off = prior + E;          // [E+1]  exclusive scan of total
-    int32_t* run = off + E + 1;        // [kWaves][E] running first rank per wave
-    __shared__ int32_t s_invalid, s_dropped;
+// LDS layout shared by both ranking kernels (int32 words).
+struct RankLds {
+    int32_t* total;  // [E]   valid entries per expert in the whole table
+    int32_t* prior;  // [E]   valid entries per expert in blocks before this one
+    int32_t* off;    // [E+1] exclusive scan of total
+    int32_t* run;    // [kRankWaves][E] running first rank per ranking wave
+};
 
+__device__ __forceinline__ RankLds carve(int32_t* sm, int E) {
+    RankLds l;
+    l.total = sm;
+    l.prior = sm + E;
+    l.off = sm + 2 * E;
+    l.run = sm + 3 * E + 1;
+    return l;
+}
+
+constexpr size_t rank_lds_bytes(int E) { return static_cast<size_t>(3 * E + 1 + kRankWaves * E) * 4; }
+
+// Everything after total/prior/num_invalid are known (all threads call it).
+__device__ void finish_layout(const int32_t* __restrict__ idx, int64_t n, int E, int cap,
+                              int chunk, int nblocks, int64_t R, RankLds l, int32_t num_invalid,
+                              int32_t* s_dropped, int32_t* __restrict__ count,
+                              int32_t* __restrict__ offset, int32_t* __restrict__ slot_of,
+                              int32_t* __restrict__ src_of_slot, int32_t* __restrict__ status) {
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const uint32_t lane = lane_id();
 
-    // 1. Column sums of the block-histogram table, eight rows in flight.
-    for (int e = tid; e <= E; e += kThreads) {
+    // Exclusive scan of total into off (wave 0; each lane owns a run of
+    // consecutive experts), and the number of entries dropped by the capacity.
+    if (wave == 0) {
+        const int per = (E + kWave - 1) / kWave;
+        const int e0 = min(E, static_cast<int>(lane) * per);
+        const int e1 = min(E, e0 + per);
+        int32_t local = 0, drop = 0;
+        for (int e = e0; e < e1; ++e) {
+            local += l.total[e];
+            if (cap > 0 && l.total[e] > cap) drop += l.total[e] - cap;
+        }
+        const int32_t incl = wave_inclusive_scan(local);
+        int32_t run_sum = incl - local;
+        for (int e = e0; e < e1; ++e) {
+            l.off[e] = run_sum;
+            run_sum += l.total[e];
+        }
+        if (lane == kWave - 1) l.off[E] = incl;
+        const int32_t drop_all = wave_inclusive_scan(drop);
+        if (lane == kWave - 1) *s_dropped = drop_all;
+    }
+    for (int e = tid; e < kRankWaves * E; e += blockDim.x) l.run[e] = 0;
+    __syncthreads();
+
+    if (b == 0) {
+        for (int e = tid; e < E; e += blockDim.x) {
+            count[e] = l.total[e];
+            offset[e] = l.off[e];
+        }
+        if (tid == 0) {
+            offset[E] = l.off[E];
+            status[0] = num_invalid;
+            status[1] = *s_dropped;
+        }
+    }
+
+    // Per-wave histograms of this block's entries.  Ranking wave w owns the
+    // contiguous run [begin + w*S, begin + (w+1)*S).
+    const int nbits = key_bits(E);
+    const int64_t begin = static_cast<int64_t>(b) * chunk;
+    const int64_t end = (begin + chunk < n) ? begin + chunk : n;
+    const int S = chunk / kRankWaves;
+    const int64_t wbegin = begin + static_cast<int64_t>(wave) * S;
+    int32_t* wrun = l.run + wave * E;
+    if (wave < kRankWaves) {
+        for (int step = 0; step < S; step += kWave) {
+            const int64_t i = wbegin + step + lane;
+            const bool in = i < end;
+            const int32_t key = in ? idx[i] : -1;
+            const bool valid = in && valid_id(key, E);
+            const uint64_t peers = match_peers(valid ? key : 0, nbits, __ballot(valid));
+            if (valid && (peers & lanemask_lt()) == 0) wrun[key] += __popcll(peers);
+        }
+    }
+    __syncthreads();
+
+    // First rank of each (wave, expert): entries in earlier blocks, then in
+    // earlier waves of this block.  For the contiguous layout the expert's
+    // offset is folded in, so the value is directly a receive row; for the
+    // fixed-capacity layout it stays the rank inside the expert.
+    for (int e = tid; e < E; e += blockDim.x) {
+        int32_t acc = l.prior[e] + (cap == 0 ? l.off[e] : 0);
+        for (int w = 0; w < kRankWaves; ++w) {
+            const int32_t c = l.run[w * E + e];
+            l.run[w * E + e] = acc;
+            acc += c;
+        }
+    }
+    __syncthreads();
+
+    // Rank pass in (t, j) order: lane rank among same-expert lanes below it.
+    if (wave < kRankWaves) {
+        for (int step = 0; step < S; step += kWave) {
+            const int64_t i = wbegin + step + lane;
+            const bool in = i < end;
+            const int32_t key = in ? idx[i] : -1;
+            const bool valid = in && valid_id(key, E);
+            const uint64_t peers = match_peers(valid ? key : 0, nbits, __ballot(valid));
+            int32_t first = 0;
+            if (valid) first = wrun[key];
+            if (valid && (peers & lanemask_lt()) == 0) wrun[key] = first + __popcll(peers);
+            if (in) {
+                int32_t slot = -1;
+                if (valid) {
+                    const int32_t r = first + __popcll(peers & lanemask_lt());
+                    if (cap == 0) {
+                        slot = r;
+                    } else if (r < cap) {
+                        slot = key * cap + r;
+                    }
+                }
+                slot_of[i] = slot;
+                if (slot >= 0 && slot < R) src_of_slot[slot] = static_cast<int32_t>(i);
+            }
+        }
+    }
+
+    // Receive rows that no entry fills get src_of_slot = -1.
+    const int64_t gtid = static_cast<int64_t>(b) * blockDim.x + tid;
+    const int64_t gstride = static_cast<int64_t>(nblocks) * blockDim.x;
+    if (cap == 0) {
+        for (int64_t r = l.off[E] + gtid; r < R; r += gstride) src_of_slot[r] = -1;
+    } else {
+        for (int64_t r = gtid; r < R; r += gstride) {
+            const int e = static_cast<int>(r / cap);
+            const int rr = static_cast<int>(r - static_cast<int64_t>(e) * cap);
+            if (rr >= min(l.total[e], cap)) src_of_slot[r] = -1;
+        }
+    }
+}
+
+// ---- single-pass path --------------------------------------------------------
+
+__global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(
+        const int32_t* __restrict__ idx, int64_t n, int E, int cap, int chunk, int nblocks,
+        int64_t R, int32_t* __restrict__ count, int32_t* __restrict__ offset,
+        int32_t* __restrict__ slot_of, int32_t* __restrict__ src_of_slot,
+        int32_t* __restrict__ status) {
+    extern __shared__ int32_t sm[];
+    __shared__ int32_t s_invalid, s_dropped;
+    const RankLds l = carve(sm, E);
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += kSingleThreads) {
+        l.total[e] = 0;
+        l.prior[e] = 0;
+    }
+    if (tid == 0) s_invalid = 0;
+    __syncthreads();
+
+    // Whole-table histogram, and the histogram of the entries before this
+    // block.
+    const int64_t begin = static_cast<int64_t>(blockIdx.x) * chunk;
+    int32_t invalid = 0;
+    for (int64_t base = 0; base < n; base += 4 * kSingleThreads) {
+        int32_t key[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = base + u * kSingleThreads + tid;
+            key[u] = (i < n) ? idx[i] : E;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = base + u * kSingleThreads + tid;
+            if (valid_id(key[u], E)) {
+                atomicAdd(&l.total[key[u]], 1);
+                if (i < begin) atomicAdd(&l.prior[key[u]], 1);
+            } else if (i < n) {
+                ++invalid;
+            }
+        }
+    }
+    if (invalid) atomicAdd(&s_invalid, invalid);
+    __syncthreads();
+
+    finish_layout(idx, n, E, cap, chunk, nblocks, R, l, s_invalid, &s_dropped, count, offset,
+                  slot_of, src_of_slot, status);
+}
+
+// ---- two-pass path -----------------------------------------------------------
+
+__global__ __launch_bounds__(kRankThreads) void layout_hist_kernel(
+        const int32_t* __restrict__ idx, int64_t n, int E, int chunk,
+        int32_t* __restrict__ block_hist) {
+    extern __shared__ int32_t hist[];  // [E + 1]; hist[E] counts invalid ids
+    const int b = blockIdx.x;
+    for (int e = threadIdx.x; e <= E; e += kRankThreads) hist[e] = 0;
+    __syncthreads();
+
+    const int nbits = key_bits(E);
+    const int64_t begin = static_cast<int64_t>(b) * chunk;
+    const int64_t end = (begin + chunk < n) ? begin + chunk : n;
+    for (int64_t base = begin; base < begin + chunk; base += kRankThreads) {
+        const int64_t i = base + threadIdx.x;
+        const bool in = i < end;
+        const int32_t key = in ? idx[i] : -1;
+        const bool valid = in && valid_id(key, E);
+        const uint64_t peers = match_peers(valid ? key : 0, nbits, __ballot(valid));
+        if (valid && (peers & lanemask_lt()) == 0) atomicAdd(&hist[key], __popcll(peers));
+        const uint64_t invalid = __ballot(in && !valid);
+        if (lane_id() == 0 && invalid) atomicAdd(&hist[E], __popcll(invalid));
+    }
+    __syncthreads();
+    int32_t* row = block_hist + static_cast<int64_t>(b) * (E + 1);
+    for (int e = threadIdx.x; e <= E; e += kRankThreads) row[e] = hist[e];
+}
+
+__global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
+        const int32_t* __restrict__ idx, int64_t n, int E, int cap, int chunk, int nblocks,
+        int64_t R, const int32_t* __restrict__ block_hist, int32_t* __restrict__ count,
+        int32_t* __restrict__ offset, int32_t* __restrict__ slot_of,
+        int32_t* __restrict__ src_of_slot, int32_t* __restrict__ status) {
+    extern __shared__ int32_t sm[];
+    __shared__ int32_t s_invalid, s_dropped;
+    const RankLds l = carve(sm, E);
+    const int b = blockIdx.x;
+
+    // Column sums of the block-histogram table, eight rows in flight.
+    for (int e = threadIdx.x; e <= E; e += kRankThreads) {
         int32_t tot = 0, pre = 0;
         int bb = 0;
         for (; bb + 8 <= nblocks; bb += 8) {
@@ -115,120 +307,16 @@ __global__ __launch_bounds__(kThreads) void layout_rank_kernel(
             pre += (bb < b) ? v : 0;
         }
         if (e < E) {
-            total[e] = tot;
-            prior[e] = pre;
+            l.total[e] = tot;
+            l.prior[e] = pre;
         } else {
             s_invalid = tot;
         }
     }
     __syncthreads();
 
-    // 2. Exclusive scan of total into off (wave 0; each lane owns a run of
-    //    consecutive experts), and the number dropped by the capacity.
-    if (wave == 0) {
-        const int per = (E + kWave - 1) / kWave;
-        const int e0 = min(E, static_cast<int>(lane) * per);
-        const int e1 = min(E, e0 + per);
-        int32_t local = 0, drop = 0;
-        for (int e = e0; e < e1; ++e) {
-            local += total[e];
-            if (cap > 0 && total[e] > cap) drop += total[e] - cap;
-        }
-        const int32_t incl = wave_inclusive_scan(local);
-        int32_t run_sum = incl - local;
-        for (int e = e0; e < e1; ++e) {
-            off[e] = run_sum;
-            run_sum += total[e];
-        }
-        if (lane == kWave - 1) off[E] = incl;
-        const int32_t drop_all = wave_inclusive_scan(drop);
-        if (lane == kWave - 1) s_dropped = drop_all;
-    }
-    __syncthreads();
-
-    if (b == 0) {
-        for (int e = tid; e < E; e += kThreads) {
-            count[e] = total[e];
-            offset[e] = off[e];
-        }
-        if (tid == 0) {
-            offset[E] = off[E];
-            status[0] = s_invalid;
-            status[1] = s_dropped;
-        }
-    }
-
-    // 3. Per-wave histograms of this block's chunk.  Wave w owns the
-    //    contiguous sub-chunk [begin + w*S, begin + (w+1)*S).
-    const int nbits = key_bits(E);
-    const int64_t begin = static_cast<int64_t>(b) * chunk;
-    const int64_t end = (begin + chunk < n) ? begin + chunk : n;
-    const int S = chunk / kWaves;
-    const int64_t wbegin = begin + static_cast<int64_t>(wave) * S;
-    int32_t* wrun = run + wave * E;
-    for (int e = tid; e < kWaves * E; e += kThreads) run[e] = 0;
-    __syncthreads();
-    for (int step = 0; step < S; step += kWave) {
-        const int64_t i = wbegin + step + lane;
-        const bool in = i < end;
-        const int32_t key = in ? idx[i] : -1;
-        const bool valid = in && static_cast<uint32_t>(key) < static_cast<uint32_t>(E);
-        const uint64_t peers = match_peers(valid ? key : 0, nbits, __ballot(valid));
-        if (valid && (peers & lanemask_lt()) == 0) wrun[key] += __popcll(peers);
-    }
-    __syncthreads();
-
-    // 4. First rank of each (wave, expert): entries in earlier blocks, then in
-    //    earlier waves of this block.  For the contiguous layout the expert's
-    //    offset is folded in, so the value is directly a receive row; for the
-    //    fixed-capacity layout it stays the rank inside the expert.
-    for (int e = tid; e < E; e += kThreads) {
-        int32_t acc = prior[e] + (cap == 0 ? off[e] : 0);
-        for (int w = 0; w < kWaves; ++w) {
-            const int32_t c = run[w * E + e];
-            run[w * E + e] = acc;
-            acc += c;
-        }
-    }
-    __syncthreads();
-
-    // 5. Rank pass in (t, j) order: lane rank among same-expert lanes below it.
-    for (int step = 0; step < S; step += kWave) {
-        const int64_t i = wbegin + step + lane;
-        const bool in = i < end;
-        const int32_t key = in ? idx[i] : -1;
-        const bool valid = in && static_cast<uint32_t>(key) < static_cast<uint32_t>(E);
-        const uint64_t peers = match_peers(valid ? key : 0, nbits, __ballot(valid));
-        int32_t first = 0;
-        if (valid) first = wrun[key];
-        if (valid && (peers & lanemask_lt()) == 0) wrun[key] = first + __popcll(peers);
-        if (in) {
-            int32_t slot = -1;
-            if (valid) {
-                const int32_t r = first + __popcll(peers & lanemask_lt());
-                if (cap == 0) {
-                    slot = r;
-                } else if (r < cap) {
-                    slot = key * cap + r;
-                }
-            }
-            slot_of[i] = slot;
-            if (slot >= 0 && slot < R) src_of_slot[slot] = static_cast<int32_t>(i);
-        }
-    }
-
-    // 6. Receive rows that no entry fills get src_of_slot = -1.
-    const int64_t gtid = static_cast<int64_t>(b) * kThreads + tid;
-    const int64_t gstride = static_cast<int64_t>(nblocks) * kThreads;
-    if (cap == 0) {
-        for (int64_t r = off[E] + gtid; r < R; r += gstride) src_of_slot[r] = -1;
-    } else {
-        for (int64_t r = gtid; r < R; r += gstride) {
-            const int e = static_cast<int>(r / cap);
-            const int rr = static_cast<int>(r - static_cast<int64_t>(e) * cap);
-            if (rr >= min(total[e], cap)) src_of_slot[r] = -1;
-        }
-    }
+    finish_layout(idx, n, E, cap, chunk, nblocks, R, l, s_invalid, &s_dropped, count, offset,
+                  slot_of, src_of_slot, status);
 }
 
 }  // namespace
@@ -236,38 +324,49 @@ __global__ __launch_bounds__(kThreads) void layout_rank_kernel(
 LayoutGeometry layout_geometry(const ep_problem& p) {
     LayoutGeometry g;
     g.entries = static_cast<int64_t>(p.num_tokens) * p.num_topk;
-    // Aim for at most ~32 blocks so that each block's column sums stay short,
-    // with 1..64 entries per thread.
-    constexpr int64_t kTargetBlocks = 32;
-    int64_t per_thread = (g.entries + static_cast<int64_t>(kThreads) * kTargetBlocks - 1) /
-                         (static_cast<int64_t>(kThreads) * kTargetBlocks);
-    if (per_thread < 1) per_thread = 1;
-    if (per_thread > 64) per_thread = 64;
-    g.chunk = static_cast<int32_t>(per_thread * kThreads);
-    int64_t blocks = (g.entries + g.chunk - 1) / g.chunk;
+    g.single_pass = g.entries <= kSinglePassMaxEntries;
+    // Single pass: about 2048 entries per workgroup (at most 64 workgroups),
+    // since every workgroup pays for the whole-table histogram.  Two passes:
+    // about 32 workgroups so each column sum stays short.  Chunks are
+    // multiples of kRankThreads so every ranking wave owns whole 64-entry steps.
+    const int64_t target_blocks = g.single_pass ? 64 : 32;
+    const int64_t min_chunk = g.single_pass ? 2048 : kRankThreads;
+    int64_t chunk = (g.entries + target_blocks - 1) / target_blocks;
+    if (chunk < min_chunk) chunk = min_chunk;
+    chunk = ((chunk + kRankThreads - 1) / kRankThreads) * kRankThreads;
+    g.chunk = static_cast<int32_t>(chunk);
+    const int64_t blocks = (g.entries + chunk - 1) / chunk;
     g.blocks = static_cast<int32_t>(blocks < 1 ? 1 : blocks);
     return g;
 }
 
 int64_t layout_workspace_bytes(const ep_problem& p) {
     const LayoutGeometry g = layout_geometry(p);
-    const int64_t bytes = static_cast<int64_t>(g.blocks) * (p.num_experts + 1) * 4;
-    return ((bytes + 255) / 256) * 256;
+    const int64_t bytes =
+        g.single_pass ? 0 : static_cast<int64_t>(g.blocks) * (p.num_experts + 1) * 4;
+    const int64_t rounded = ((bytes + 255) / 256) * 256;
+    return rounded < 256 ? 256 : rounded;
 }
 
 hipError_t launch_layout(const ep_problem& p, const int32_t* topk_idx, const ep_layout_t& out,
                          int32_t* block_hist, hipStream_t stream) {
     const LayoutGeometry g = layout_geometry(p);
     const int E = p.num_experts;
-    const int64_t R = (p.capacity == 0) ? g.entries
-                                        : static_cast<int64_t>(E) * p.capacity;
+    const int64_t R = (p.capacity == 0) ? g.entries : static_cast<int64_t>(E) * p.capacity;
+    if (g.single_pass) {
+        hipLaunchKernelGGL(layout_single_kernel, dim3(g.blocks), dim3(kSingleThreads),
+                           rank_lds_bytes(E), stream, topk_idx, g.entries, E, p.capacity,
+                           g.chunk, g.blocks, R, out.count, out.offset, out.slot_of,
+                           out.src_of_slot, out.status);
+        return hipGetLastError();
+    }
     const size_t lds_hist = static_cast<size_t>(E + 1) * 4;
-    hipLaunchKernelGGL(layout_hist_kernel, dim3(g.blocks), dim3(kThreads), lds_hist, stream,
+    hipLaunchKernelGGL(layout_hist_kernel, dim3(g.blocks), dim3(kRankThreads), lds_hist, stream,
                        topk_idx, g.entries, E, g.chunk, block_hist);
-    const size_t lds_rank = static_cast<size_t>(3 * E + 1 + kWaves * E) * 4;
-    hipLaunchKernelGGL(layout_rank_kernel, dim3(g.blocks), dim3(kThreads), lds_rank, stream,
-                       topk_idx, g.entries, E, p.capacity, g.chunk, g.blocks, R, block_hist,
-                       out.count, out.offset, out.slot_of, out.src_of_slot, out.status);
+    hipLaunchKernelGGL(layout_rank_kernel, dim3(g.blocks), dim3(kRankThreads),
+                       rank_lds_bytes(E), stream, topk_idx, g.entries, E, p.capacity, g.chunk,
+                       g.blocks, R, block_hist, out.count, out.offset, out.slot_of,
+                       out.src_of_slot, out.status);
     return hipGetLastError();
 }
 
