@@ -74,7 +74,7 @@ int ep_layout(const ep_problem* prob, const int32_t* topk_idx, const ep_layout_t
     if (rc != EP_OK) return rc;
     if (static_cast<int64_t>(prob->num_tokens) * prob->num_topk > 0 && topk_idx == nullptr)
         return EP_ERR_ARG;
-    if (!aligned4(topk_idx)) return EP_ERR_ALIGN;
+    if (!aligned16(topk_idx)) return EP_ERR_ALIGN;
     if (workspace == nullptr ||
         static_cast<int64_t>(workspace_bytes) < ep::layout_workspace_bytes(*prob))
         return EP_ERR_ARG;

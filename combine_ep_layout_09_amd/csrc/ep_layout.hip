@@ -189,15 +189,14 @@ __device__ void finish_layout(const int32_t* __restrict__ idx, int64_t n, int E,
     }
 
     // Receive rows that no entry fills get src_of_slot = -1.
-    const int64_t gtid = static_cast<int64_t>(b) * blockDim.x + tid;
-    const int64_t gstride = static_cast<int64_t>(nblocks) * blockDim.x;
     if (cap == 0) {
+        const int64_t gtid = static_cast<int64_t>(b) * blockDim.x + tid;
+        const int64_t gstride = static_cast<int64_t>(nblocks) * blockDim.x;
         for (int64_t r = l.off[E] + gtid; r < R; r += gstride) src_of_slot[r] = -1;
     } else {
-        for (int64_t r = gtid; r < R; r += gstride) {
-            const int e = static_cast<int>(r / cap);
-            const int rr = static_cast<int>(r - static_cast<int64_t>(e) * cap);
-            if (rr >= min(l.total[e], cap)) src_of_slot[r] = -1;
+        for (int e = b; e < E; e += nblocks) {
+            int32_t* rows = src_of_slot + static_cast<int64_t>(e) * cap;
+            for (int r = min(l.total[e], cap) + tid; r < cap; r += blockDim.x) rows[r] = -1;
         }
     }
 }
@@ -221,24 +220,40 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(
     __syncthreads();
 
     // Whole-table histogram, and the histogram of the entries before this
-    // block.
+    // block.  Each lane reads 16-byte groups of 4 entries, kGroups groups in
+    // flight per pass (idx is 16-byte aligned; the last, partial group is read
+    // entry by entry).
+    constexpr int kGroups = 8;
     const int64_t begin = static_cast<int64_t>(blockIdx.x) * chunk;
+    const int64_t ngroups = (n + 3) / 4;
+    const int4* idx4 = reinterpret_cast<const int4*>(idx);
     int32_t invalid = 0;
-    for (int64_t base = 0; base < n; base += 4 * kSingleThreads) {
-        int32_t key[4];
+    for (int64_t g0 = 0; g0 < ngroups; g0 += kGroups * kSingleThreads) {
+        int4 q[kGroups];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t i = base + u * kSingleThreads + tid;
-            key[u] = (i < n) ? idx[i] : E;
+        for (int u = 0; u < kGroups; ++u) {
+            const int64_t g = g0 + u * kSingleThreads + tid;
+            if (4 * g + 3 < n) {
+                q[u] = idx4[g];
+            } else {
+                q[u].x = (4 * g + 0 < n) ? idx[4 * g + 0] : E;
+                q[u].y = (4 * g + 1 < n) ? idx[4 * g + 1] : E;
+                q[u].z = (4 * g + 2 < n) ? idx[4 * g + 2] : E;
+                q[u].w = E;
+            }
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t i = base + u * kSingleThreads + tid;
-            if (valid_id(key[u], E)) {
-                atomicAdd(&l.total[key[u]], 1);
-                if (i < begin) atomicAdd(&l.prior[key[u]], 1);
-            } else if (i < n) {
-                ++invalid;
+        for (int u = 0; u < kGroups; ++u) {
+            const int64_t i0 = 4 * (g0 + u * kSingleThreads + tid);
+            const int32_t key[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (valid_id(key[c], E)) {
+                    atomicAdd(&l.total[key[c]], 1);
+                    if (i0 + c < begin) atomicAdd(&l.prior[key[c]], 1);
+                } else if (i0 + c < n) {
+                    ++invalid;
+                }
             }
         }
     }
@@ -325,12 +340,12 @@ LayoutGeometry layout_geometry(const ep_problem& p) {
     LayoutGeometry g;
     g.entries = static_cast<int64_t>(p.num_tokens) * p.num_topk;
     g.single_pass = g.entries <= kSinglePassMaxEntries;
-    // Single pass: about 2048 entries per workgroup (at most 64 workgroups),
-    // since every workgroup pays for the whole-table histogram.  Two passes:
-    // about 32 workgroups so each column sum stays short.  Chunks are
-    // multiples of kRankThreads so every ranking wave owns whole 64-entry steps.
+    // Single pass: up to 64 workgroups (each pays for the whole-table
+    // histogram, so more would only add L2 traffic).  Two passes: about 32
+    // workgroups so each column sum stays short.  Chunks are multiples of
+    // kRankThreads so every ranking wave owns whole 64-entry steps.
     const int64_t target_blocks = g.single_pass ? 64 : 32;
-    const int64_t min_chunk = g.single_pass ? 2048 : kRankThreads;
+    const int64_t min_chunk = kRankThreads;
     int64_t chunk = (g.entries + target_blocks - 1) / target_blocks;
     if (chunk < min_chunk) chunk = min_chunk;
     chunk = ((chunk + kRankThreads - 1) / kRankThreads) * kRankThreads;

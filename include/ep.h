@@ -44,8 +44,8 @@
  *   R = number of receive rows = T*k (contiguous) or E*cap (fixed capacity).
  *   All tensors are dense, row-major, in device memory (HBM) unless noted.
  *   bf16 data is passed as 16-bit patterns, E4M3FN data as bytes.
- *   Data pointers (x, recv_x, recv_scales, expert_out, y) must be 16-byte
- *   aligned.
+ *   Data pointers (x, recv_x, recv_scales, expert_out, y) and topk_idx must
+ *   be 16-byte aligned; the other int32 / fp32 arrays 4-byte aligned.
  *
  * Ownership.  The caller allocates and owns every buffer, including the
  * layout workspace.  The library never allocates, frees, or keeps a pointer
@@ -120,7 +120,8 @@ int64_t ep_num_recv_rows(const ep_problem* prob);
 int64_t ep_layout_workspace_bytes(const ep_problem* prob);
 
 /* Routing layout.
- *   topk_idx   int32 [T, k], device.  Expert id of each routing entry.
+ *   topk_idx   int32 [T, k], device, 16-byte aligned.  Expert id of each
+ *              routing entry.
  *   out        host struct of device pointers, all written:
  *              count, offset, slot_of, src_of_slot (every one of the R rows
  *              is written, -1 for rows no entry fills), status.

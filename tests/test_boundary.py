@@ -93,6 +93,7 @@ def test_null_and_alignment_checks():
     assert lib.ep_layout(P, FAKE, ctypes.byref(_layout_struct(count=None)), FAKE, ws, None) == ep.EP_ERR_ARG
     assert lib.ep_layout(P, FAKE, ctypes.byref(_layout_struct(slot_of=FAKE + 2)), FAKE, ws, None) == ep.EP_ERR_ALIGN
     assert lib.ep_layout(P, FAKE + 1, ctypes.byref(_layout_struct()), FAKE, ws, None) == ep.EP_ERR_ALIGN
+    assert lib.ep_layout(P, FAKE + 4, ctypes.byref(_layout_struct()), FAKE, ws, None) == ep.EP_ERR_ALIGN
     assert lib.ep_layout(P, FAKE, ctypes.byref(_layout_struct()), FAKE, ws - 1, None) == ep.EP_ERR_ARG
     assert lib.ep_layout(P, FAKE, ctypes.byref(_layout_struct()), None, ws, None) == ep.EP_ERR_ARG
     assert lib.ep_layout(P, FAKE, ctypes.byref(_layout_struct()), FAKE + 8, ws, None) == ep.EP_ERR_ALIGN
