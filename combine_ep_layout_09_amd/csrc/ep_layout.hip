@@ -12,15 +12,18 @@
 // before it can rank is, per expert, the number of valid entries in the whole
 // table (for the offsets) and in the blocks before its own (for the ranks).
 //
-// Single-pass path (tables up to kSinglePassMaxEntries entries, which covers
-// every decode and prefill batch in practice): one kernel.  Every workgroup
-// reads the whole routing table -- at most a few hundred KiB, served from L2
-// after the first touch -- and builds both histograms itself with LDS atomics.
-// No workgroup waits on another, so the kernel has no inter-block
-// synchronisation at all and costs one launch.
+// Single-pass path (tables up to kSinglePassMaxEntries entries: decode-sized
+// batches): one kernel.  Every workgroup reads the whole routing table and
+// builds both histograms itself with LDS atomics.  No workgroup waits on
+// another, so there is no inter-block synchronisation and one launch.  LDS
+// atomics cost about one wave instruction per 64 entries per workgroup, which
+// is why this path stops at small tables.
 //
 // Two-pass path (larger tables): layout_hist writes each block's histogram to
-// the workspace, and layout_rank sums the table's columns.
+// a column-major table in the workspace; layout_rank reads, per expert, the
+// whole column at once (at most 64 blocks, so 16 loads of 16 bytes in flight
+// per thread) and splits it at its own block.  The kernel boundary is the only
+// synchronisation between blocks.
 //
 // Both paths then run the same tail: wave 0 scans the totals into offsets;
 // workgroup 0 writes count, offset and status; the block's entries are split
@@ -39,7 +42,8 @@ namespace {
 constexpr int kRankWaves = 4;                 // waves that rank a block's entries
 constexpr int kRankThreads = kRankWaves * kWave;
 constexpr int kSingleThreads = 1024;          // single-pass workgroup
-constexpr int64_t kSinglePassMaxEntries = 1 << 18;
+constexpr int64_t kSinglePassMaxEntries = 8192;   // whole-table LDS histogram per workgroup
+constexpr int kTwoPassMaxBlocks = 64;
 
 __device__ __forceinline__ int key_bits(int E) {
     // number of bits needed for ids 0..E-1
@@ -266,8 +270,12 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(
 
 // ---- two-pass path -----------------------------------------------------------
 
+// Column-major block-histogram table: column e (e = E counts invalid ids)
+// holds one count per block, padded to a multiple of 4 blocks.
+__host__ __device__ constexpr int table_stride(int nblocks) { return (nblocks + 3) & ~3; }
+
 __global__ __launch_bounds__(kRankThreads) void layout_hist_kernel(
-        const int32_t* __restrict__ idx, int64_t n, int E, int chunk,
+        const int32_t* __restrict__ idx, int64_t n, int E, int chunk, int nblocks,
         int32_t* __restrict__ block_hist) {
     extern __shared__ int32_t hist[];  // [E + 1]; hist[E] counts invalid ids
     const int b = blockIdx.x;
@@ -288,8 +296,13 @@ __global__ __launch_bounds__(kRankThreads) void layout_hist_kernel(
         if (lane_id() == 0 && invalid) atomicAdd(&hist[E], __popcll(invalid));
     }
     __syncthreads();
-    int32_t* row = block_hist + static_cast<int64_t>(b) * (E + 1);
-    for (int e = threadIdx.x; e <= E; e += kRankThreads) row[e] = hist[e];
+    const int stride = table_stride(nblocks);
+    for (int e = threadIdx.x; e <= E; e += kRankThreads) {
+        block_hist[static_cast<int64_t>(e) * stride + b] = hist[e];
+        // zero the padding so column sums can read whole 16-byte groups
+        if (b == nblocks - 1)
+            for (int p = nblocks; p < stride; ++p) block_hist[static_cast<int64_t>(e) * stride + p] = 0;
+    }
 }
 
 __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
@@ -302,24 +315,28 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     const RankLds l = carve(sm, E);
     const int b = blockIdx.x;
 
-    // Column sums of the block-histogram table, eight rows in flight.
+    // Column sums of the block-histogram table: each thread reads its whole
+    // column (16-byte groups, all in flight) and splits it at this block.
+    constexpr int kMaxGroups = kTwoPassMaxBlocks / 4;
+    const int stride = table_stride(nblocks);
+    const int ngroups = stride / 4;
     for (int e = threadIdx.x; e <= E; e += kRankThreads) {
+        const int4* col = reinterpret_cast<const int4*>(block_hist + static_cast<int64_t>(e) * stride);
+        int4 q[kMaxGroups];
+#pragma unroll
+        for (int g = 0; g < kMaxGroups; ++g)
+            if (g < ngroups) q[g] = col[g];
         int32_t tot = 0, pre = 0;
-        int bb = 0;
-        for (; bb + 8 <= nblocks; bb += 8) {
-            int32_t v[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = block_hist[static_cast<int64_t>(bb + q) * (E + 1) + e];
+        for (int g = 0; g < kMaxGroups; ++g) {
+            if (g < ngroups) {
+                const int32_t v[4] = {q[g].x, q[g].y, q[g].z, q[g].w};
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                tot += v[q];
-                pre += (bb + q < b) ? v[q] : 0;
+                for (int c = 0; c < 4; ++c) {
+                    tot += v[c];
+                    pre += (4 * g + c < b) ? v[c] : 0;
+                }
             }
-        }
-        for (; bb < nblocks; ++bb) {
-            const int32_t v = block_hist[static_cast<int64_t>(bb) * (E + 1) + e];
-            tot += v;
-            pre += (bb < b) ? v : 0;
         }
         if (e < E) {
             l.total[e] = tot;
@@ -340,11 +357,11 @@ LayoutGeometry layout_geometry(const ep_problem& p) {
     LayoutGeometry g;
     g.entries = static_cast<int64_t>(p.num_tokens) * p.num_topk;
     g.single_pass = g.entries <= kSinglePassMaxEntries;
-    // Single pass: up to 64 workgroups (each pays for the whole-table
-    // histogram, so more would only add L2 traffic).  Two passes: about 32
-    // workgroups so each column sum stays short.  Chunks are multiples of
-    // kRankThreads so every ranking wave owns whole 64-entry steps.
-    const int64_t target_blocks = g.single_pass ? 64 : 32;
+    // Up to 64 workgroups (single pass: each pays for the whole-table
+    // histogram; two passes: each reads a 64-entry column per expert).
+    // Chunks are multiples of kRankThreads so every ranking wave owns whole
+    // 64-entry steps.
+    const int64_t target_blocks = kTwoPassMaxBlocks;
     const int64_t min_chunk = kRankThreads;
     int64_t chunk = (g.entries + target_blocks - 1) / target_blocks;
     if (chunk < min_chunk) chunk = min_chunk;
@@ -358,7 +375,7 @@ LayoutGeometry layout_geometry(const ep_problem& p) {
 int64_t layout_workspace_bytes(const ep_problem& p) {
     const LayoutGeometry g = layout_geometry(p);
     const int64_t bytes =
-        g.single_pass ? 0 : static_cast<int64_t>(g.blocks) * (p.num_experts + 1) * 4;
+        g.single_pass ? 0 : static_cast<int64_t>(table_stride(g.blocks)) * (p.num_experts + 1) * 4;
     const int64_t rounded = ((bytes + 255) / 256) * 256;
     return rounded < 256 ? 256 : rounded;
 }
@@ -377,7 +394,7 @@ hipError_t launch_layout(const ep_problem& p, const int32_t* topk_idx, const ep_
     }
     const size_t lds_hist = static_cast<size_t>(E + 1) * 4;
     hipLaunchKernelGGL(layout_hist_kernel, dim3(g.blocks), dim3(kRankThreads), lds_hist, stream,
-                       topk_idx, g.entries, E, g.chunk, block_hist);
+                       topk_idx, g.entries, E, g.chunk, g.blocks, block_hist);
     hipLaunchKernelGGL(layout_rank_kernel, dim3(g.blocks), dim3(kRankThreads),
                        rank_lds_bytes(E), stream, topk_idx, g.entries, E, p.capacity, g.chunk,
                        g.blocks, R, block_hist, out.count, out.offset, out.slot_of,

@@ -184,9 +184,10 @@ EDGE = [
     dict(T=2500, H=256, k=6, E=7, cap=3, fp8=True, name="capacity_overflow"),
     dict(T=50, H=2304, k=4, E=16, cap=64, fp8=False, name="capacity_bf16_no_overflow"),
     # routing tables around the size where the layout switches from one kernel
-    # to two (2^18 entries)
-    dict(T=32768, H=128, k=8, E=64, cap=0, fp8=True, name="layout_single_pass_largest"),
-    dict(T=32769, H=128, k=8, E=64, cap=0, fp8=False, name="layout_two_pass_smallest"),
+    # to two (8192 entries), and a large two-pass table
+    dict(T=1024, H=128, k=8, E=64, cap=0, fp8=True, name="layout_single_pass_largest"),
+    dict(T=1025, H=136, k=8, E=64, cap=0, fp8=False, name="layout_two_pass_smallest"),
+    dict(T=1171, H=128, k=7, E=1000, cap=0, fp8=False, name="layout_two_pass_many_experts"),
     dict(T=40000, H=128, k=8, E=256, cap=1500, fp8=True, name="layout_two_pass_capacity"),
 ]
 
