@@ -82,12 +82,54 @@ __device__ __forceinline__ RankLds carve(int32_t* sm, int E) {
     return l;
 }
 
-constexpr size_t rank_lds_bytes(int E) { return static_cast<size_t>(3 * E + 1 + kRankWaves * E) * 4; }
+constexpr int rank_lds_words(int E) { return ((3 * E + 1 + kRankWaves * E) + 3) & ~3; }
+constexpr int kStageMax = 4096;   // block entries staged in LDS (16 KiB)
+// rank LDS + the staged entries of the block when they fit
+constexpr size_t rank_lds_bytes(int E, int chunk) {
+    return static_cast<size_t>(rank_lds_words(E) + (chunk <= kStageMax ? chunk : 0)) * 4;
+}
+
+// Reads 16-byte groups of routing entries [4g, 4g+4) (entries at or past
+// `end` read as -1).  idx is 16-byte aligned.
+__device__ __forceinline__ int4 load_group(const int32_t* __restrict__ idx, int64_t i0, int64_t end) {
+    int4 q;
+    if (i0 + 3 < end) {
+        q = *reinterpret_cast<const int4*>(idx + i0);
+    } else {
+        q.x = (i0 + 0 < end) ? idx[i0 + 0] : -1;
+        q.y = (i0 + 1 < end) ? idx[i0 + 1] : -1;
+        q.z = (i0 + 2 < end) ? idx[i0 + 2] : -1;
+        q.w = -1;
+    }
+    return q;
+}
+
+// Copies the block's entries [begin, begin + chunk) into LDS (all loads of a
+// thread in flight together); entries past n read as -1.
+__device__ void stage_keys(const int32_t* __restrict__ idx, int64_t begin, int64_t end, int chunk,
+                           int32_t* stage) {
+    const int ng = chunk / 4;
+    for (int g0 = 0; g0 < ng; g0 += 4 * static_cast<int>(blockDim.x)) {
+        int4 q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int g = g0 + u * static_cast<int>(blockDim.x) + threadIdx.x;
+            if (g < ng) q[u] = load_group(idx, begin + 4 * g, end);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int g = g0 + u * static_cast<int>(blockDim.x) + threadIdx.x;
+            if (g < ng) reinterpret_cast<int4*>(stage)[g] = q[u];
+        }
+    }
+}
 
 // Everything after total/prior/num_invalid are known (all threads call it).
-__device__ void finish_layout(const int32_t* __restrict__ idx, int64_t n, int E, int cap,
-                              int chunk, int nblocks, int64_t R, RankLds l, int32_t num_invalid,
-                              int32_t* s_dropped, int32_t* __restrict__ count,
+// `stage` holds the block's entries when they fit in LDS, else nullptr (they
+// are then read from idx).
+__device__ void finish_layout(const int32_t* __restrict__ idx, const int32_t* stage, int64_t n,
+                              int E, int cap, int chunk, int nblocks, int64_t R, RankLds l,
+                              int32_t num_invalid, int32_t* s_dropped, int32_t* __restrict__ count,
                               int32_t* __restrict__ offset, int32_t* __restrict__ slot_of,
                               int32_t* __restrict__ src_of_slot, int32_t* __restrict__ status) {
     const int b = blockIdx.x;
@@ -143,7 +185,7 @@ __device__ void finish_layout(const int32_t* __restrict__ idx, int64_t n, int E,
         for (int step = 0; step < S; step += kWave) {
             const int64_t i = wbegin + step + lane;
             const bool in = i < end;
-            const int32_t key = in ? idx[i] : -1;
+            const int32_t key = !in ? -1 : (stage ? stage[i - begin] : idx[i]);
             const bool valid = in && valid_id(key, E);
             const uint64_t peers = match_peers(valid ? key : 0, nbits, __ballot(valid));
             if (valid && (peers & lanemask_lt()) == 0) wrun[key] += __popcll(peers);
@@ -170,7 +212,7 @@ __device__ void finish_layout(const int32_t* __restrict__ idx, int64_t n, int E,
         for (int step = 0; step < S; step += kWave) {
             const int64_t i = wbegin + step + lane;
             const bool in = i < end;
-            const int32_t key = in ? idx[i] : -1;
+            const int32_t key = !in ? -1 : (stage ? stage[i - begin] : idx[i]);
             const bool valid = in && valid_id(key, E);
             const uint64_t peers = match_peers(valid ? key : 0, nbits, __ballot(valid));
             int32_t first = 0;
@@ -212,7 +254,7 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(
         int64_t R, int32_t* __restrict__ count, int32_t* __restrict__ offset,
         int32_t* __restrict__ slot_of, int32_t* __restrict__ src_of_slot,
         int32_t* __restrict__ status) {
-    extern __shared__ int32_t sm[];
+    extern __shared__ __align__(16) int32_t sm[];
     __shared__ int32_t s_invalid, s_dropped;
     const RankLds l = carve(sm, E);
     const int tid = threadIdx.x;
@@ -262,10 +304,15 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(
         }
     }
     if (invalid) atomicAdd(&s_invalid, invalid);
+    int32_t* stage = chunk <= kStageMax ? sm + rank_lds_words(E) : nullptr;
+    if (stage) {
+        const int64_t end = (begin + chunk < n) ? begin + chunk : n;
+        stage_keys(idx, begin, end, chunk, stage);
+    }
     __syncthreads();
 
-    finish_layout(idx, n, E, cap, chunk, nblocks, R, l, s_invalid, &s_dropped, count, offset,
-                  slot_of, src_of_slot, status);
+    finish_layout(idx, stage, n, E, cap, chunk, nblocks, R, l, s_invalid, &s_dropped, count,
+                  offset, slot_of, src_of_slot, status);
 }
 
 // ---- two-pass path -----------------------------------------------------------
@@ -282,19 +329,29 @@ __global__ __launch_bounds__(kRankThreads) void layout_hist_kernel(
     for (int e = threadIdx.x; e <= E; e += kRankThreads) hist[e] = 0;
     __syncthreads();
 
-    const int nbits = key_bits(E);
     const int64_t begin = static_cast<int64_t>(b) * chunk;
     const int64_t end = (begin + chunk < n) ? begin + chunk : n;
-    for (int64_t base = begin; base < begin + chunk; base += kRankThreads) {
-        const int64_t i = base + threadIdx.x;
-        const bool in = i < end;
-        const int32_t key = in ? idx[i] : -1;
-        const bool valid = in && valid_id(key, E);
-        const uint64_t peers = match_peers(valid ? key : 0, nbits, __ballot(valid));
-        if (valid && (peers & lanemask_lt()) == 0) atomicAdd(&hist[key], __popcll(peers));
-        const uint64_t invalid = __ballot(in && !valid);
-        if (lane_id() == 0 && invalid) atomicAdd(&hist[E], __popcll(invalid));
+    const int ng = chunk / 4;
+    int32_t invalid = 0;
+    for (int g0 = 0; g0 < ng; g0 += 4 * kRankThreads) {
+        int4 q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int g = g0 + u * kRankThreads + threadIdx.x;
+            q[u] = (g < ng) ? load_group(idx, begin + 4 * g, end) : make_int4(-1, -1, -1, -1);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i0 = begin + 4 * (g0 + u * kRankThreads + threadIdx.x);
+            const int32_t key[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (valid_id(key[c], E)) atomicAdd(&hist[key[c]], 1);
+                else if (i0 + c < end) ++invalid;
+            }
+        }
     }
+    if (invalid) atomicAdd(&hist[E], invalid);
     __syncthreads();
     const int stride = table_stride(nblocks);
     for (int e = threadIdx.x; e <= E; e += kRankThreads) {
@@ -310,10 +367,14 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
         int64_t R, const int32_t* __restrict__ block_hist, int32_t* __restrict__ count,
         int32_t* __restrict__ offset, int32_t* __restrict__ slot_of,
         int32_t* __restrict__ src_of_slot, int32_t* __restrict__ status) {
-    extern __shared__ int32_t sm[];
+    extern __shared__ __align__(16) int32_t sm[];
     __shared__ int32_t s_invalid, s_dropped;
     const RankLds l = carve(sm, E);
     const int b = blockIdx.x;
+    const int64_t begin = static_cast<int64_t>(b) * chunk;
+    const int64_t end = (begin + chunk < n) ? begin + chunk : n;
+    int32_t* stage = chunk <= kStageMax ? sm + rank_lds_words(E) : nullptr;
+    if (stage) stage_keys(idx, begin, end, chunk, stage);
 
     // Column sums of the block-histogram table: each thread reads its whole
     // column (16-byte groups, all in flight) and splits it at this block.
@@ -347,8 +408,8 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     }
     __syncthreads();
 
-    finish_layout(idx, n, E, cap, chunk, nblocks, R, l, s_invalid, &s_dropped, count, offset,
-                  slot_of, src_of_slot, status);
+    finish_layout(idx, stage, n, E, cap, chunk, nblocks, R, l, s_invalid, &s_dropped, count,
+                  offset, slot_of, src_of_slot, status);
 }
 
 }  // namespace
@@ -387,8 +448,8 @@ hipError_t launch_layout(const ep_problem& p, const int32_t* topk_idx, const ep_
     const int64_t R = (p.capacity == 0) ? g.entries : static_cast<int64_t>(E) * p.capacity;
     if (g.single_pass) {
         hipLaunchKernelGGL(layout_single_kernel, dim3(g.blocks), dim3(kSingleThreads),
-                           rank_lds_bytes(E), stream, topk_idx, g.entries, E, p.capacity,
-                           g.chunk, g.blocks, R, out.count, out.offset, out.slot_of,
+                           rank_lds_bytes(E, g.chunk), stream, topk_idx, g.entries, E,
+                           p.capacity, g.chunk, g.blocks, R, out.count, out.offset, out.slot_of,
                            out.src_of_slot, out.status);
         return hipGetLastError();
     }
@@ -396,7 +457,7 @@ hipError_t launch_layout(const ep_problem& p, const int32_t* topk_idx, const ep_
     hipLaunchKernelGGL(layout_hist_kernel, dim3(g.blocks), dim3(kRankThreads), lds_hist, stream,
                        topk_idx, g.entries, E, g.chunk, g.blocks, block_hist);
     hipLaunchKernelGGL(layout_rank_kernel, dim3(g.blocks), dim3(kRankThreads),
-                       rank_lds_bytes(E), stream, topk_idx, g.entries, E, p.capacity, g.chunk,
+                       rank_lds_bytes(E, g.chunk), stream, topk_idx, g.entries, E, p.capacity, g.chunk,
                        g.blocks, R, block_hist, out.count, out.offset, out.slot_of,
                        out.src_of_slot, out.status);
     return hipGetLastError();
