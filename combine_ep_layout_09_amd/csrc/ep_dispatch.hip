@@ -10,8 +10,8 @@
 // Launch shape: one workgroup per (token, column tile).  A lane owns VPL
 // 16-byte pieces of the row, spaced one workgroup-width apart so that every
 // load and store instruction of a wave covers 1 KiB of contiguous memory.
-// The host picks the workgroup width so that a tile covers the row with as
-// little slack as possible; lanes past the end of the row redo the last piece
+// Tiles are two waves wide with VPL chosen so a tile covers a whole row of up
+// to 8192 channels; lanes past the end of the row redo the last piece
 // (last 16-lane group for FP8) and store the same bytes to the same place,
 // which keeps the loads free of branches.  All VPL loads are issued before
 // any store, the row is read from HBM once however large k is, and the
@@ -166,6 +166,40 @@ TileShape row_tile_shape(int nvec, int vpl) {
     return {((per_tile + 63) / 64) * 64, tiles};
 }
 
+namespace {
+
+// Dispatch tiles are two waves wide with up to eight 16-byte pieces per lane,
+// so one workgroup covers a whole row of up to 1024 pieces (H = 8192 bf16);
+// the pieces of a lane are all loaded before the first store.
+struct DispatchShape {
+    int vpl;
+    TileShape tile;
+};
+
+DispatchShape dispatch_shape(int nvec) {
+    if (nvec <= 128) return {1, {((nvec + 63) / 64) * 64, 1}};
+    const int vpl = nvec >= 1024 ? 8 : (nvec + 127) / 128;
+    return {vpl, {128, (nvec + 128 * vpl - 1) / (128 * vpl)}};
+}
+
+template <int VPL>
+void launch_vpl(const ep_problem& p, dim3 grid, int threads, const void* x, int nvec,
+                const int32_t* slot_of, int64_t R, void* recv_x, float* recv_scales,
+                hipStream_t stream) {
+    if (p.use_fp8) {
+        const size_t lds = static_cast<size_t>(threads) * VPL / 16 * 4;
+        hipLaunchKernelGGL(dispatch_fp8_kernel<VPL>, grid, dim3(threads), lds, stream,
+                           static_cast<const u32x4*>(x), nvec, p.hidden / 128, p.num_topk,
+                           slot_of, R, static_cast<u32x2*>(recv_x), recv_scales);
+    } else {
+        hipLaunchKernelGGL(dispatch_bf16_kernel<VPL>, grid, dim3(threads), 0, stream,
+                           static_cast<const u32x4*>(x), nvec, p.num_topk, slot_of, R,
+                           static_cast<u32x4*>(recv_x));
+    }
+}
+
+}  // namespace
+
 hipError_t launch_dispatch(const ep_problem& p, const void* x, const int32_t* slot_of,
                            void* recv_x, float* recv_scales, hipStream_t stream) {
     const int T = p.num_tokens;
@@ -173,18 +207,18 @@ hipError_t launch_dispatch(const ep_problem& p, const void* x, const int32_t* sl
     const int nvec = p.hidden / 8;
     const int64_t R = p.capacity == 0 ? static_cast<int64_t>(T) * p.num_topk
                                       : static_cast<int64_t>(p.num_experts) * p.capacity;
-    constexpr int kVpl = 2;
-    const TileShape s = row_tile_shape(nvec, kVpl);
-    const dim3 grid(T, s.tiles);
-    if (p.use_fp8) {
-        const size_t lds = static_cast<size_t>(s.threads) * kVpl / 16 * 4;
-        hipLaunchKernelGGL(dispatch_fp8_kernel<kVpl>, grid, dim3(s.threads), lds, stream,
-                           static_cast<const u32x4*>(x), nvec, p.hidden / 128, p.num_topk,
-                           slot_of, R, static_cast<u32x2*>(recv_x), recv_scales);
-    } else {
-        hipLaunchKernelGGL(dispatch_bf16_kernel<kVpl>, grid, dim3(s.threads), 0, stream,
-                           static_cast<const u32x4*>(x), nvec, p.num_topk, slot_of, R,
-                           static_cast<u32x4*>(recv_x));
+    const DispatchShape ds = dispatch_shape(nvec);
+    const dim3 grid(T, ds.tile.tiles);
+    const int th = ds.tile.threads;
+    switch (ds.vpl) {
+        case 1: launch_vpl<1>(p, grid, th, x, nvec, slot_of, R, recv_x, recv_scales, stream); break;
+        case 2: launch_vpl<2>(p, grid, th, x, nvec, slot_of, R, recv_x, recv_scales, stream); break;
+        case 3: launch_vpl<3>(p, grid, th, x, nvec, slot_of, R, recv_x, recv_scales, stream); break;
+        case 4: launch_vpl<4>(p, grid, th, x, nvec, slot_of, R, recv_x, recv_scales, stream); break;
+        case 5: launch_vpl<5>(p, grid, th, x, nvec, slot_of, R, recv_x, recv_scales, stream); break;
+        case 6: launch_vpl<6>(p, grid, th, x, nvec, slot_of, R, recv_x, recv_scales, stream); break;
+        case 7: launch_vpl<7>(p, grid, th, x, nvec, slot_of, R, recv_x, recv_scales, stream); break;
+        default: launch_vpl<8>(p, grid, th, x, nvec, slot_of, R, recv_x, recv_scales, stream); break;
     }
     return hipGetLastError();
 }

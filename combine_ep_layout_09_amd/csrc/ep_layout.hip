@@ -362,7 +362,13 @@ __global__ __launch_bounds__(kRankThreads) void layout_hist_kernel(
     }
 }
 
-__global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
+// Workgroup width of layout_rank: one thread per expert column (at least the
+// four ranking waves).
+__host__ __device__ constexpr int rank_threads(int E) {
+    return E <= kRankThreads ? kRankThreads : ((E + kWave - 1) / kWave) * kWave;
+}
+
+__global__ __launch_bounds__(1024) void layout_rank_kernel(
         const int32_t* __restrict__ idx, int64_t n, int E, int cap, int chunk, int nblocks,
         int64_t R, const int32_t* __restrict__ block_hist, int32_t* __restrict__ count,
         int32_t* __restrict__ offset, int32_t* __restrict__ slot_of,
@@ -371,22 +377,43 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     __shared__ int32_t s_invalid, s_dropped;
     const RankLds l = carve(sm, E);
     const int b = blockIdx.x;
+    const int tid = threadIdx.x;
     const int64_t begin = static_cast<int64_t>(b) * chunk;
     const int64_t end = (begin + chunk < n) ? begin + chunk : n;
     int32_t* stage = chunk <= kStageMax ? sm + rank_lds_words(E) : nullptr;
-    if (stage) stage_keys(idx, begin, end, chunk, stage);
 
-    // Column sums of the block-histogram table: each thread reads its whole
-    // column (16-byte groups, all in flight) and splits it at this block.
+    // Every global load of the prologue is issued before any is used, so the
+    // prologue costs one memory latency: this block's entries (at most four
+    // 16-byte groups per thread), one whole table column per thread for
+    // experts 0..E-1 (at most 16 groups), and the invalid-id column spread
+    // over the first lanes of wave 0.
     constexpr int kMaxGroups = kTwoPassMaxBlocks / 4;
+    const int ng = stage ? chunk / 4 : 0;
     const int stride = table_stride(nblocks);
     const int ngroups = stride / 4;
-    for (int e = threadIdx.x; e <= E; e += kRankThreads) {
-        const int4* col = reinterpret_cast<const int4*>(block_hist + static_cast<int64_t>(e) * stride);
-        int4 q[kMaxGroups];
+    int4 keys[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int g = u * static_cast<int>(blockDim.x) + tid;
+        if (g < ng) keys[u] = load_group(idx, begin + 4 * g, end);
+    }
+    int4 q[kMaxGroups];
+    if (tid < E) {
+        const int4* col = reinterpret_cast<const int4*>(block_hist + static_cast<int64_t>(tid) * stride);
 #pragma unroll
         for (int g = 0; g < kMaxGroups; ++g)
             if (g < ngroups) q[g] = col[g];
+    }
+    int4 qi = make_int4(0, 0, 0, 0);
+    if (tid < ngroups)
+        qi = reinterpret_cast<const int4*>(block_hist + static_cast<int64_t>(E) * stride)[tid];
+
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int g = u * static_cast<int>(blockDim.x) + tid;
+        if (g < ng) reinterpret_cast<int4*>(stage)[g] = keys[u];
+    }
+    if (tid < E) {
         int32_t tot = 0, pre = 0;
 #pragma unroll
         for (int g = 0; g < kMaxGroups; ++g) {
@@ -399,12 +426,12 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
                 }
             }
         }
-        if (e < E) {
-            l.total[e] = tot;
-            l.prior[e] = pre;
-        } else {
-            s_invalid = tot;
-        }
+        l.total[tid] = tot;
+        l.prior[tid] = pre;
+    }
+    if (tid < kWave) {
+        const int32_t inv = wave_inclusive_scan(qi.x + qi.y + qi.z + qi.w);
+        if (tid == kWave - 1) s_invalid = inv;
     }
     __syncthreads();
 
@@ -456,7 +483,7 @@ hipError_t launch_layout(const ep_problem& p, const int32_t* topk_idx, const ep_
     const size_t lds_hist = static_cast<size_t>(E + 1) * 4;
     hipLaunchKernelGGL(layout_hist_kernel, dim3(g.blocks), dim3(kRankThreads), lds_hist, stream,
                        topk_idx, g.entries, E, g.chunk, g.blocks, block_hist);
-    hipLaunchKernelGGL(layout_rank_kernel, dim3(g.blocks), dim3(kRankThreads),
+    hipLaunchKernelGGL(layout_rank_kernel, dim3(g.blocks), dim3(rank_threads(E)),
                        rank_lds_bytes(E, g.chunk), stream, topk_idx, g.entries, E, p.capacity, g.chunk,
                        g.blocks, R, block_hist, out.count, out.offset, out.slot_of,
                        out.src_of_slot, out.status);
