@@ -168,15 +168,19 @@ TileShape row_tile_shape(int nvec, int vpl) {
 
 namespace {
 
-// Dispatch tiles are two waves wide with up to eight 16-byte pieces per lane,
-// so one workgroup covers a whole row of up to 1024 pieces (H = 8192 bf16);
-// the pieces of a lane are all loaded before the first store.
+// For batches of 1024 tokens or more, dispatch tiles are two waves wide with
+// up to eight 16-byte pieces per lane, so one workgroup covers a whole row of
+// up to 1024 pieces (H = 8192 bf16); the pieces of a lane are all loaded before
+// the first store.
 struct DispatchShape {
     int vpl;
     TileShape tile;
 };
 
-DispatchShape dispatch_shape(int nvec) {
+DispatchShape dispatch_shape(int nvec, int T) {
+    // Few tokens (decode batches): wide workgroups, one piece per lane, so
+    // that enough waves exist to keep HBM busy.
+    if (T < 1024) return {1, row_tile_shape(nvec, 1)};
     if (nvec <= 128) return {1, {((nvec + 63) / 64) * 64, 1}};
     const int vpl = nvec >= 1024 ? 8 : (nvec + 127) / 128;
     return {vpl, {128, (nvec + 128 * vpl - 1) / (128 * vpl)}};
@@ -207,7 +211,7 @@ hipError_t launch_dispatch(const ep_problem& p, const void* x, const int32_t* sl
     const int nvec = p.hidden / 8;
     const int64_t R = p.capacity == 0 ? static_cast<int64_t>(T) * p.num_topk
                                       : static_cast<int64_t>(p.num_experts) * p.capacity;
-    const DispatchShape ds = dispatch_shape(nvec);
+    const DispatchShape ds = dispatch_shape(nvec, T);
     const dim3 grid(T, ds.tile.tiles);
     const int th = ds.tile.threads;
     switch (ds.vpl) {

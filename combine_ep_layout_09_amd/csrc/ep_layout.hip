@@ -39,8 +39,9 @@
 namespace ep {
 namespace {
 
-constexpr int kRankWaves = 4;                 // waves that rank a block's entries
-constexpr int kRankThreads = kRankWaves * kWave;
+constexpr int kHistThreads = 256;             // layout_hist workgroup
+constexpr int kRankThreads = 1024;            // layout_rank / layout_single workgroup
+constexpr int kRankRunWords = 4096;           // LDS words for the per-wave running ranks
 constexpr int kSingleThreads = 1024;          // single-pass workgroup
 constexpr int64_t kSinglePassMaxEntries = 8192;   // whole-table LDS histogram per workgroup
 constexpr int kTwoPassMaxBlocks = 64;
@@ -70,7 +71,7 @@ struct RankLds {
     int32_t* total;  // [E]   valid entries per expert in the whole table
     int32_t* prior;  // [E]   valid entries per expert in blocks before this one
     int32_t* off;    // [E+1] exclusive scan of total
-    int32_t* run;    // [kRankWaves][E] running first rank per ranking wave
+    int32_t* run;    // [rank waves][E] running first rank per ranking wave
 };
 
 __device__ __forceinline__ RankLds carve(int32_t* sm, int E) {
@@ -82,7 +83,15 @@ __device__ __forceinline__ RankLds carve(int32_t* sm, int E) {
     return l;
 }
 
-constexpr int rank_lds_words(int E) { return ((3 * E + 1 + kRankWaves * E) + 3) & ~3; }
+// Waves that rank a block's entries: as many as the workgroup has, as long as
+// their running-rank rows fit in kRankRunWords.
+__host__ __device__ constexpr int rank_waves(int E) {
+    return (kRankRunWords / E >= kRankThreads / kWave) ? kRankThreads / kWave
+           : (kRankRunWords / E >= 4 ? kRankRunWords / E : 4);
+}
+__host__ __device__ constexpr int rank_lds_words(int E) {
+    return ((3 * E + 1 + rank_waves(E) * E) + 3) & ~3;
+}
 constexpr int kStageMax = 4096;   // block entries staged in LDS (16 KiB)
 // rank LDS + the staged entries of the block when they fit
 constexpr size_t rank_lds_bytes(int E, int chunk) {
@@ -158,7 +167,8 @@ __device__ void finish_layout(const int32_t* __restrict__ idx, const int32_t* st
         const int32_t drop_all = wave_inclusive_scan(drop);
         if (lane == kWave - 1) *s_dropped = drop_all;
     }
-    for (int e = tid; e < kRankWaves * E; e += blockDim.x) l.run[e] = 0;
+    const int rw = rank_waves(E);
+    for (int e = tid; e < rw * E; e += blockDim.x) l.run[e] = 0;
     __syncthreads();
 
     if (b == 0) {
@@ -174,14 +184,15 @@ __device__ void finish_layout(const int32_t* __restrict__ idx, const int32_t* st
     }
 
     // Per-wave histograms of this block's entries.  Ranking wave w owns the
-    // contiguous run [begin + w*S, begin + (w+1)*S).
+    // contiguous run [begin + w*S, begin + (w+1)*S), S a multiple of 64;
+    // runs past the end of the block are empty.
     const int nbits = key_bits(E);
     const int64_t begin = static_cast<int64_t>(b) * chunk;
     const int64_t end = (begin + chunk < n) ? begin + chunk : n;
-    const int S = chunk / kRankWaves;
+    const int S = ((chunk / rw + kWave - 1) / kWave) * kWave;
     const int64_t wbegin = begin + static_cast<int64_t>(wave) * S;
     int32_t* wrun = l.run + wave * E;
-    if (wave < kRankWaves) {
+    if (wave < rw) {
         for (int step = 0; step < S; step += kWave) {
             const int64_t i = wbegin + step + lane;
             const bool in = i < end;
@@ -199,7 +210,7 @@ __device__ void finish_layout(const int32_t* __restrict__ idx, const int32_t* st
     // fixed-capacity layout it stays the rank inside the expert.
     for (int e = tid; e < E; e += blockDim.x) {
         int32_t acc = l.prior[e] + (cap == 0 ? l.off[e] : 0);
-        for (int w = 0; w < kRankWaves; ++w) {
+        for (int w = 0; w < rw; ++w) {
             const int32_t c = l.run[w * E + e];
             l.run[w * E + e] = acc;
             acc += c;
@@ -208,7 +219,7 @@ __device__ void finish_layout(const int32_t* __restrict__ idx, const int32_t* st
     __syncthreads();
 
     // Rank pass in (t, j) order: lane rank among same-expert lanes below it.
-    if (wave < kRankWaves) {
+    if (wave < rw) {
         for (int step = 0; step < S; step += kWave) {
             const int64_t i = wbegin + step + lane;
             const bool in = i < end;
@@ -321,28 +332,28 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(
 // holds one count per block, padded to a multiple of 4 blocks.
 __host__ __device__ constexpr int table_stride(int nblocks) { return (nblocks + 3) & ~3; }
 
-__global__ __launch_bounds__(kRankThreads) void layout_hist_kernel(
+__global__ __launch_bounds__(kHistThreads) void layout_hist_kernel(
         const int32_t* __restrict__ idx, int64_t n, int E, int chunk, int nblocks,
         int32_t* __restrict__ block_hist) {
     extern __shared__ int32_t hist[];  // [E + 1]; hist[E] counts invalid ids
     const int b = blockIdx.x;
-    for (int e = threadIdx.x; e <= E; e += kRankThreads) hist[e] = 0;
+    for (int e = threadIdx.x; e <= E; e += kHistThreads) hist[e] = 0;
     __syncthreads();
 
     const int64_t begin = static_cast<int64_t>(b) * chunk;
     const int64_t end = (begin + chunk < n) ? begin + chunk : n;
     const int ng = chunk / 4;
     int32_t invalid = 0;
-    for (int g0 = 0; g0 < ng; g0 += 4 * kRankThreads) {
+    for (int g0 = 0; g0 < ng; g0 += 4 * kHistThreads) {
         int4 q[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int g = g0 + u * kRankThreads + threadIdx.x;
+            const int g = g0 + u * kHistThreads + threadIdx.x;
             q[u] = (g < ng) ? load_group(idx, begin + 4 * g, end) : make_int4(-1, -1, -1, -1);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int64_t i0 = begin + 4 * (g0 + u * kRankThreads + threadIdx.x);
+            const int64_t i0 = begin + 4 * (g0 + u * kHistThreads + threadIdx.x);
             const int32_t key[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -354,18 +365,12 @@ __global__ __launch_bounds__(kRankThreads) void layout_hist_kernel(
     if (invalid) atomicAdd(&hist[E], invalid);
     __syncthreads();
     const int stride = table_stride(nblocks);
-    for (int e = threadIdx.x; e <= E; e += kRankThreads) {
+    for (int e = threadIdx.x; e <= E; e += kHistThreads) {
         block_hist[static_cast<int64_t>(e) * stride + b] = hist[e];
         // zero the padding so column sums can read whole 16-byte groups
         if (b == nblocks - 1)
             for (int p = nblocks; p < stride; ++p) block_hist[static_cast<int64_t>(e) * stride + p] = 0;
     }
-}
-
-// Workgroup width of layout_rank: one thread per expert column (at least the
-// four ranking waves).
-__host__ __device__ constexpr int rank_threads(int E) {
-    return E <= kRankThreads ? kRankThreads : ((E + kWave - 1) / kWave) * kWave;
 }
 
 __global__ __launch_bounds__(1024) void layout_rank_kernel(
@@ -447,13 +452,13 @@ LayoutGeometry layout_geometry(const ep_problem& p) {
     g.single_pass = g.entries <= kSinglePassMaxEntries;
     // Up to 64 workgroups (single pass: each pays for the whole-table
     // histogram; two passes: each reads a 64-entry column per expert).
-    // Chunks are multiples of kRankThreads so every ranking wave owns whole
-    // 64-entry steps.
+    // Chunks are multiples of 256 entries (16-byte groups of the histogram
+    // kernel, whole 64-entry ranking steps).
     const int64_t target_blocks = kTwoPassMaxBlocks;
-    const int64_t min_chunk = kRankThreads;
+    const int64_t min_chunk = 256;
     int64_t chunk = (g.entries + target_blocks - 1) / target_blocks;
     if (chunk < min_chunk) chunk = min_chunk;
-    chunk = ((chunk + kRankThreads - 1) / kRankThreads) * kRankThreads;
+    chunk = ((chunk + 255) / 256) * 256;
     g.chunk = static_cast<int32_t>(chunk);
     const int64_t blocks = (g.entries + chunk - 1) / chunk;
     g.blocks = static_cast<int32_t>(blocks < 1 ? 1 : blocks);
@@ -481,9 +486,9 @@ hipError_t launch_layout(const ep_problem& p, const int32_t* topk_idx, const ep_
         return hipGetLastError();
     }
     const size_t lds_hist = static_cast<size_t>(E + 1) * 4;
-    hipLaunchKernelGGL(layout_hist_kernel, dim3(g.blocks), dim3(kRankThreads), lds_hist, stream,
+    hipLaunchKernelGGL(layout_hist_kernel, dim3(g.blocks), dim3(kHistThreads), lds_hist, stream,
                        topk_idx, g.entries, E, g.chunk, g.blocks, block_hist);
-    hipLaunchKernelGGL(layout_rank_kernel, dim3(g.blocks), dim3(rank_threads(E)),
+    hipLaunchKernelGGL(layout_rank_kernel, dim3(g.blocks), dim3(kRankThreads),
                        rank_lds_bytes(E, g.chunk), stream, topk_idx, g.entries, E, p.capacity, g.chunk,
                        g.blocks, R, block_hist, out.count, out.offset, out.slot_of,
                        out.src_of_slot, out.status);
