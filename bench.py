@@ -16,8 +16,8 @@ HBM peak, with its duration measured by HIP events recorded around each
 kernel call on the stream it runs on, over a second run of K steps.  `cpu_baseline` times the CPU oracle
 on the same inputs (serial, one core).
 
-  python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config 3]
-                  [--no-cpu-baseline] [--cpu-seconds 12]
+  python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 3]
+                  [--no-cpu-baseline] [--cpu-seconds 12] [--copy-calibration]
 """
 import argparse
 import hashlib
@@ -155,11 +155,14 @@ def cpu_baseline(wl, eo_host, bytes_total, target_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run one device-to-device copy of 256 MiB (for scaling "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -177,6 +180,14 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        a = torch.ones(256 << 20, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": a.numel()}))
+        return 0
     print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
     wl = workloads.make(args.config)
     eo_host = wl.expert_out()
