@@ -55,14 +55,25 @@ __device__ __forceinline__ bool valid_id(int32_t key, int E) {
     return static_cast<uint32_t>(key) < static_cast<uint32_t>(E);
 }
 
-// Inclusive scan across the 64 lanes of a wave.
+// Inclusive integer scans on DPP lane moves (no LDS traffic).  row_shr by
+// 1, 2, 4, 8 scans each row of 16 lanes (lanes shifted in from outside the
+// row read 0); row_bcast 15 and 31 then carry row totals into later rows.
+constexpr int kDppRowShr = 0x110;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+__device__ __forceinline__ int32_t row16_inclusive_scan(int32_t v) {
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr | 1, 0xf, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr | 2, 0xf, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr | 4, 0xf, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr | 8, 0xf, 0xf, false);
+    return v;
+}
+
 __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v) {
-    const uint32_t lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int32_t t = __shfl_up(v, d);
-        if (lane >= static_cast<uint32_t>(d)) v += t;
-    }
+    v = row16_inclusive_scan(v);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xa, 0xf, false);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xc, 0xf, false);
     return v;
 }
 
@@ -207,14 +218,16 @@ __device__ void finish_layout(const int32_t* __restrict__ idx, const int32_t* st
     // First rank of each (wave, expert): entries in earlier blocks, then in
     // earlier waves of this block.  For the contiguous layout the expert's
     // offset is folded in, so the value is directly a receive row; for the
-    // fixed-capacity layout it stays the rank inside the expert.
-    for (int e = tid; e < E; e += blockDim.x) {
-        int32_t acc = l.prior[e] + (cap == 0 ? l.off[e] : 0);
-        for (int w = 0; w < rw; ++w) {
-            const int32_t c = l.run[w * E + e];
-            l.run[w * E + e] = acc;
-            acc += c;
-        }
+    // fixed-capacity layout it stays the rank inside the expert.  Each
+    // 16-lane row takes one expert, lane w holding wave w's count, and an
+    // exclusive row scan gives every wave its start (rw <= 16).
+    for (int e0 = 0; e0 < E; e0 += static_cast<int>(blockDim.x) / 16) {
+        const int e = e0 + tid / 16;
+        const int w = tid & 15;
+        const bool mine = e < E && w < rw;
+        const int32_t c = mine ? l.run[w * E + e] : 0;
+        const int32_t before = row16_inclusive_scan(c) - c;
+        if (mine) l.run[w * E + e] = l.prior[e] + (cap == 0 ? l.off[e] : 0) + before;
     }
     __syncthreads();
 
