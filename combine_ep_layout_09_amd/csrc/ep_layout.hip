@@ -95,13 +95,15 @@ __device__ __forceinline__ RankLds carve(int32_t* sm, int E) {
 }
 
 // Waves that rank a block's entries: as many as the workgroup has, as long as
-// their running-rank rows fit in kRankRunWords.
+// their running-rank rows fit in kRankRunWords.  Rows are E+1 words apart so
+// that the 16 lanes reading one expert across 16 waves hit 16 different LDS
+// banks.
 __host__ __device__ constexpr int rank_waves(int E) {
-    return (kRankRunWords / E >= kRankThreads / kWave) ? kRankThreads / kWave
-           : (kRankRunWords / E >= 4 ? kRankRunWords / E : 4);
+    return (kRankRunWords / (E + 1) >= kRankThreads / kWave) ? kRankThreads / kWave
+           : (kRankRunWords / (E + 1) >= 4 ? kRankRunWords / (E + 1) : 4);
 }
 __host__ __device__ constexpr int rank_lds_words(int E) {
-    return ((3 * E + 1 + rank_waves(E) * E) + 3) & ~3;
+    return ((3 * E + 1 + rank_waves(E) * (E + 1)) + 3) & ~3;
 }
 constexpr int kStageMax = 4096;   // block entries staged in LDS (16 KiB)
 // rank LDS + the staged entries of the block when they fit
@@ -179,7 +181,8 @@ __device__ void finish_layout(const int32_t* __restrict__ idx, const int32_t* st
         if (lane == kWave - 1) *s_dropped = drop_all;
     }
     const int rw = rank_waves(E);
-    for (int e = tid; e < rw * E; e += blockDim.x) l.run[e] = 0;
+    const int rs = E + 1;  // row stride of l.run
+    for (int e = tid; e < rw * rs; e += blockDim.x) l.run[e] = 0;
     __syncthreads();
 
     if (b == 0) {
@@ -202,7 +205,7 @@ __device__ void finish_layout(const int32_t* __restrict__ idx, const int32_t* st
     const int64_t end = (begin + chunk < n) ? begin + chunk : n;
     const int S = ((chunk / rw + kWave - 1) / kWave) * kWave;
     const int64_t wbegin = begin + static_cast<int64_t>(wave) * S;
-    int32_t* wrun = l.run + wave * E;
+    int32_t* wrun = l.run + wave * rs;
     if (wave < rw) {
         for (int step = 0; step < S; step += kWave) {
             const int64_t i = wbegin + step + lane;
@@ -225,9 +228,9 @@ __device__ void finish_layout(const int32_t* __restrict__ idx, const int32_t* st
         const int e = e0 + tid / 16;
         const int w = tid & 15;
         const bool mine = e < E && w < rw;
-        const int32_t c = mine ? l.run[w * E + e] : 0;
+        const int32_t c = mine ? l.run[w * rs + e] : 0;
         const int32_t before = row16_inclusive_scan(c) - c;
-        if (mine) l.run[w * E + e] = l.prior[e] + (cap == 0 ? l.off[e] : 0) + before;
+        if (mine) l.run[w * rs + e] = l.prior[e] + (cap == 0 ? l.off[e] : 0) + before;
     }
     __syncthreads();
 
@@ -342,8 +345,9 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(
 // ---- two-pass path -----------------------------------------------------------
 
 // Column-major block-histogram table: column e (e = E counts invalid ids)
-// holds one count per block, padded to a multiple of 4 blocks.
-__host__ __device__ constexpr int table_stride(int nblocks) { return (nblocks + 3) & ~3; }
+// holds one count per block, padded with zeros to kTwoPassMaxBlocks, so a
+// column is 16 groups of 16 bytes: one DPP row of 16 lanes.
+constexpr int kTableStride = kTwoPassMaxBlocks;
 
 __global__ __launch_bounds__(kHistThreads) void layout_hist_kernel(
         const int32_t* __restrict__ idx, int64_t n, int E, int chunk, int nblocks,
@@ -377,12 +381,12 @@ __global__ __launch_bounds__(kHistThreads) void layout_hist_kernel(
     }
     if (invalid) atomicAdd(&hist[E], invalid);
     __syncthreads();
-    const int stride = table_stride(nblocks);
     for (int e = threadIdx.x; e <= E; e += kHistThreads) {
-        block_hist[static_cast<int64_t>(e) * stride + b] = hist[e];
-        // zero the padding so column sums can read whole 16-byte groups
+        block_hist[static_cast<int64_t>(e) * kTableStride + b] = hist[e];
+        // zero the padding so column sums can read whole columns
         if (b == nblocks - 1)
-            for (int p = nblocks; p < stride; ++p) block_hist[static_cast<int64_t>(e) * stride + p] = 0;
+            for (int p = nblocks; p < kTableStride; ++p)
+                block_hist[static_cast<int64_t>(e) * kTableStride + p] = 0;
     }
 }
 
@@ -402,54 +406,63 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
 
     // Every global load of the prologue is issued before any is used, so the
     // prologue costs one memory latency: this block's entries (at most four
-    // 16-byte groups per thread), one whole table column per thread for
-    // experts 0..E-1 (at most 16 groups), and the invalid-id column spread
-    // over the first lanes of wave 0.
-    constexpr int kMaxGroups = kTwoPassMaxBlocks / 4;
+    // 16-byte groups per thread) and the whole table.  The table is read as
+    // 1 KiB per wave instruction: 16 lanes (a DPP row) cover one column, 4
+    // columns per instruction, and a row reduction gives the column's total
+    // and its part before this block.
+    constexpr int kColsPerLoad = kWave / 16;
     const int ng = stage ? chunk / 4 : 0;
-    const int stride = table_stride(nblocks);
-    const int ngroups = stride / 4;
+    const int ncols = E + 1;
+    const int loads_per_wave =
+        (ncols + kColsPerLoad * (kRankThreads / kWave) - 1) / (kColsPerLoad * (kRankThreads / kWave));
     int4 keys[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int g = u * static_cast<int>(blockDim.x) + tid;
+        const int g = u * kRankThreads + tid;
         if (g < ng) keys[u] = load_group(idx, begin + 4 * g, end);
     }
-    int4 q[kMaxGroups];
-    if (tid < E) {
-        const int4* col = reinterpret_cast<const int4*>(block_hist + static_cast<int64_t>(tid) * stride);
+    constexpr int kMaxLoads = (kMaxExperts + 1 + kColsPerLoad * (kRankThreads / kWave) - 1) /
+                              (kColsPerLoad * (kRankThreads / kWave));
+    const int wave = tid / kWave;
+    const int lane = tid & (kWave - 1);
+    const int grp = lane & 15;                       // 16-byte group inside the column
+    int4 q[kMaxLoads];
 #pragma unroll
-        for (int g = 0; g < kMaxGroups; ++g)
-            if (g < ngroups) q[g] = col[g];
+    for (int m = 0; m < kMaxLoads; ++m) {
+        const int col = (m * (kRankThreads / kWave) + wave) * kColsPerLoad + lane / 16;
+        if (m < loads_per_wave && col < ncols)
+            q[m] = reinterpret_cast<const int4*>(block_hist + static_cast<int64_t>(col) * kTableStride)[grp];
+        else
+            q[m] = make_int4(0, 0, 0, 0);
     }
-    int4 qi = make_int4(0, 0, 0, 0);
-    if (tid < ngroups)
-        qi = reinterpret_cast<const int4*>(block_hist + static_cast<int64_t>(E) * stride)[tid];
 
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int g = u * static_cast<int>(blockDim.x) + tid;
+        const int g = u * kRankThreads + tid;
         if (g < ng) reinterpret_cast<int4*>(stage)[g] = keys[u];
     }
-    if (tid < E) {
-        int32_t tot = 0, pre = 0;
 #pragma unroll
-        for (int g = 0; g < kMaxGroups; ++g) {
-            if (g < ngroups) {
-                const int32_t v[4] = {q[g].x, q[g].y, q[g].z, q[g].w};
+    for (int m = 0; m < kMaxLoads; ++m) {
+        if (m < loads_per_wave) {  // uniform across the wave
+            const int col = (m * (kRankThreads / kWave) + wave) * kColsPerLoad + lane / 16;
+            const int32_t v[4] = {q[m].x, q[m].y, q[m].z, q[m].w};
+            int32_t tot = 0, pre = 0;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    tot += v[c];
-                    pre += (4 * g + c < b) ? v[c] : 0;
+            for (int c = 0; c < 4; ++c) {
+                tot += v[c];
+                pre += (4 * grp + c < b) ? v[c] : 0;
+            }
+            tot = row16_inclusive_scan(tot);
+            pre = row16_inclusive_scan(pre);
+            if (grp == 15 && col < ncols) {
+                if (col < E) {
+                    l.total[col] = tot;
+                    l.prior[col] = pre;
+                } else {
+                    s_invalid = tot;
                 }
             }
         }
-        l.total[tid] = tot;
-        l.prior[tid] = pre;
-    }
-    if (tid < kWave) {
-        const int32_t inv = wave_inclusive_scan(qi.x + qi.y + qi.z + qi.w);
-        if (tid == kWave - 1) s_invalid = inv;
     }
     __syncthreads();
 
@@ -481,7 +494,7 @@ LayoutGeometry layout_geometry(const ep_problem& p) {
 int64_t layout_workspace_bytes(const ep_problem& p) {
     const LayoutGeometry g = layout_geometry(p);
     const int64_t bytes =
-        g.single_pass ? 0 : static_cast<int64_t>(table_stride(g.blocks)) * (p.num_experts + 1) * 4;
+        g.single_pass ? 0 : static_cast<int64_t>(kTableStride) * (p.num_experts + 1) * 4;
     const int64_t rounded = ((bytes + 255) / 256) * 256;
     return rounded < 256 ? 256 : rounded;
 }
