@@ -8,30 +8,33 @@
 // "[GH-ISSUE #18] Reasons for not calling NVSHMEM public APIs?".
 //
 // The T*k entries (row-major (t, j) order) are split into blocks of `chunk`
-// consecutive entries; each workgroup ranks one block.  What a workgroup needs
-// before it can rank is, per expert, the number of valid entries in the whole
-// table (for the offsets) and in the blocks before its own (for the ranks).
+// consecutive entries; each workgroup ranks one block.  Before it can rank, a
+// workgroup needs, per expert, the number of valid entries in the whole table
+// (for the offsets) and in the blocks before its own (for the ranks).
 //
 // Single-pass path (tables up to kSinglePassMaxEntries entries: decode-sized
 // batches): one kernel.  Every workgroup reads the whole routing table and
-// builds both histograms itself with LDS atomics.  No workgroup waits on
-// another, so there is no inter-block synchronisation and one launch.  LDS
-// atomics cost about one wave instruction per 64 entries per workgroup, which
-// is why this path stops at small tables.
+// builds both histograms itself with LDS atomics; no workgroup waits on
+// another.  LDS atomics cost about one wave instruction per 64 entries per
+// workgroup, which is why this path stops at small tables.
 //
 // Two-pass path (larger tables): layout_hist writes each block's histogram to
-// a column-major table in the workspace; layout_rank reads, per expert, the
-// whole column at once (at most 64 blocks, so 16 loads of 16 bytes in flight
-// per thread) and splits it at its own block.  The kernel boundary is the only
+// a column-major table in the workspace (64 rows per column, zero padded);
+// layout_rank reads the whole table as 1 KiB per wave instruction, 16 lanes
+// (one DPP row) per column, and row-reduces each column into its total and
+// its part before this block.  The kernel boundary is the only
 // synchronisation between blocks.
 //
-// Both paths then run the same tail: wave 0 scans the totals into offsets;
-// workgroup 0 writes count, offset and status; the block's entries are split
-// into one contiguous run per ranking wave, per-wave histograms give each wave
-// its first rank per expert, and inside a wave each 64-entry step ranks a lane
-// against the lower lanes with the same expert, found with one ballot per key
-// bit.  All workgroups together mark empty receive rows with -1.  The result
-// is deterministic and independent of workgroup scheduling.
+// Ranking, in both paths: the block's entries are split into one contiguous
+// run per ranking wave.  A wave loads its run's ids into registers before
+// anything else, so its own histogram (per-wave counts in LDS) is built while
+// the table loads are still in flight.  After one barrier, wave 0 scans the
+// totals into offsets, and each expert's per-wave counts are scanned across
+// waves (one 16-lane DPP row per expert) into every wave's first rank.
+// Inside a wave, each 64-entry step ranks a lane against the lower lanes with
+// the same expert, found with one ballot per key bit.  All workgroups
+// together mark empty receive rows with -1.  The result is deterministic and
+// independent of workgroup scheduling.
 
 #include "ep_device.h"
 #include "ep_internal.h"
@@ -41,10 +44,11 @@ namespace {
 
 constexpr int kHistThreads = 256;             // layout_hist workgroup
 constexpr int kRankThreads = 1024;            // layout_rank / layout_single workgroup
-constexpr int kRankRunWords = 4096;           // LDS words for the per-wave running ranks
-constexpr int kSingleThreads = 1024;          // single-pass workgroup
-constexpr int64_t kSinglePassMaxEntries = 8192;   // whole-table LDS histogram per workgroup
+constexpr int kRankRunWords = 4112;           // LDS words for the per-wave running ranks
+constexpr int64_t kSinglePassMaxEntries = 8192;
 constexpr int kTwoPassMaxBlocks = 64;
+constexpr int kTableStride = kTwoPassMaxBlocks;  // rows per table column
+constexpr int kKeySteps = 4;                  // 64-entry steps of a run held in registers
 
 __device__ __forceinline__ int key_bits(int E) {
     // number of bits needed for ids 0..E-1
@@ -77,12 +81,25 @@ __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v) {
     return v;
 }
 
+// Waves that rank a block's entries: as many as the workgroup has (16), as
+// long as their running-rank rows fit in kRankRunWords.  Rows are E+1 words
+// apart so the 16 lanes reading one expert across 16 waves hit 16 different
+// LDS banks.
+__host__ __device__ constexpr int rank_waves(int E) {
+    return (kRankRunWords / (E + 1) >= kRankThreads / kWave) ? kRankThreads / kWave
+           : (kRankRunWords / (E + 1) >= 4 ? kRankRunWords / (E + 1) : 4);
+}
+
+__host__ __device__ constexpr size_t rank_lds_bytes(int E) {
+    return static_cast<size_t>(((3 * E + 1 + rank_waves(E) * (E + 1)) + 3) & ~3) * 4;
+}
+
 // LDS layout shared by both ranking kernels (int32 words).
 struct RankLds {
     int32_t* total;  // [E]   valid entries per expert in the whole table
     int32_t* prior;  // [E]   valid entries per expert in blocks before this one
     int32_t* off;    // [E+1] exclusive scan of total
-    int32_t* run;    // [rank waves][E] running first rank per ranking wave
+    int32_t* run;    // [rank waves][E+1] running first rank per ranking wave
 };
 
 __device__ __forceinline__ RankLds carve(int32_t* sm, int E) {
@@ -94,70 +111,109 @@ __device__ __forceinline__ RankLds carve(int32_t* sm, int E) {
     return l;
 }
 
-// Waves that rank a block's entries: as many as the workgroup has, as long as
-// their running-rank rows fit in kRankRunWords.  Rows are E+1 words apart so
-// that the 16 lanes reading one expert across 16 waves hit 16 different LDS
-// banks.
-__host__ __device__ constexpr int rank_waves(int E) {
-    return (kRankRunWords / (E + 1) >= kRankThreads / kWave) ? kRankThreads / kWave
-           : (kRankRunWords / (E + 1) >= 4 ? kRankRunWords / (E + 1) : 4);
-}
-__host__ __device__ constexpr int rank_lds_words(int E) {
-    return ((3 * E + 1 + rank_waves(E) * (E + 1)) + 3) & ~3;
-}
-constexpr int kStageMax = 4096;   // block entries staged in LDS (16 KiB)
-// rank LDS + the staged entries of the block when they fit
-constexpr size_t rank_lds_bytes(int E, int chunk) {
-    return static_cast<size_t>(rank_lds_words(E) + (chunk <= kStageMax ? chunk : 0)) * 4;
+// The contiguous run of entries one ranking wave owns:
+// [wbegin, wbegin + S) clipped to the block's end.  S is a multiple of 64 and
+// rw * S covers the block; waves at or past rw (or past the block) own nothing.
+struct Run {
+    int64_t wbegin;
+    int64_t wend;
+    int S;
+    int passes;  // passes of kKeySteps * 64 entries
+};
+
+__device__ __forceinline__ Run wave_run(int64_t begin, int64_t end, int chunk, int rw, int wave) {
+    Run r;
+    r.S = ((chunk / rw + kWave - 1) / kWave) * kWave;
+    r.wbegin = begin + static_cast<int64_t>(wave) * r.S;
+    const int64_t e = r.wbegin + r.S;
+    r.wend = (wave < rw) ? (e < end ? e : end) : r.wbegin;
+    r.passes = (r.S + kKeySteps * kWave - 1) / (kKeySteps * kWave);
+    return r;
 }
 
-// Reads 16-byte groups of routing entries [4g, 4g+4) (entries at or past
-// `end` read as -1).  idx is 16-byte aligned.
-__device__ __forceinline__ int4 load_group(const int32_t* __restrict__ idx, int64_t i0, int64_t end) {
-    int4 q;
-    if (i0 + 3 < end) {
-        q = *reinterpret_cast<const int4*>(idx + i0);
-    } else {
-        q.x = (i0 + 0 < end) ? idx[i0 + 0] : -1;
-        q.y = (i0 + 1 < end) ? idx[i0 + 1] : -1;
-        q.z = (i0 + 2 < end) ? idx[i0 + 2] : -1;
-        q.w = -1;
-    }
-    return q;
-}
-
-// Copies the block's entries [begin, begin + chunk) into LDS (all loads of a
-// thread in flight together); entries past n read as -1.
-__device__ void stage_keys(const int32_t* __restrict__ idx, int64_t begin, int64_t end, int chunk,
-                           int32_t* stage) {
-    const int ng = chunk / 4;
-    for (int g0 = 0; g0 < ng; g0 += 4 * static_cast<int>(blockDim.x)) {
-        int4 q[4];
+// Ids of one pass of a run (entry p0 + 64*s + lane); entries outside the run
+// are not loaded.
+__device__ __forceinline__ void load_pass(const int32_t* __restrict__ idx, int64_t p0,
+                                          int64_t wend, uint32_t lane, int32_t (&key)[kKeySteps]) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int g = g0 + u * static_cast<int>(blockDim.x) + threadIdx.x;
-            if (g < ng) q[u] = load_group(idx, begin + 4 * g, end);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int g = g0 + u * static_cast<int>(blockDim.x) + threadIdx.x;
-            if (g < ng) reinterpret_cast<int4*>(stage)[g] = q[u];
-        }
+    for (int s = 0; s < kKeySteps; ++s) {
+        const int64_t i = p0 + s * kWave + lane;
+        key[s] = (i < wend) ? idx[i] : -1;
     }
 }
 
-// Everything after total/prior/num_invalid are known (all threads call it).
-// `stage` holds the block's entries when they fit in LDS, else nullptr (they
-// are then read from idx).
-__device__ void finish_layout(const int32_t* __restrict__ idx, const int32_t* stage, int64_t n,
-                              int E, int cap, int chunk, int nblocks, int64_t R, RankLds l,
-                              int32_t num_invalid, int32_t* s_dropped, int32_t* __restrict__ count,
+// Adds one pass of this wave's ids to its running-count row.
+__device__ __forceinline__ void count_pass(const int32_t (&key)[kKeySteps], int64_t p0,
+                                           int64_t wend, uint32_t lane, int E, int nbits,
+                                           int32_t* wrun) {
+#pragma unroll
+    for (int s = 0; s < kKeySteps; ++s) {
+        const int64_t i = p0 + s * kWave + lane;
+        const bool valid = i < wend && valid_id(key[s], E);
+        const uint64_t peers = match_peers(valid ? key[s] : 0, nbits, __ballot(valid));
+        if (valid && (peers & lanemask_lt()) == 0) wrun[key[s]] += __popcll(peers);
+    }
+}
+
+// Ranks one pass of this wave's entries, writing slot_of and src_of_slot.
+__device__ __forceinline__ void rank_pass(const int32_t (&key)[kKeySteps], int64_t p0,
+                                          int64_t wend, uint32_t lane, int E, int cap,
+                                          int nbits, int64_t R, int32_t* wrun,
+                                          int32_t* __restrict__ slot_of,
+                                          int32_t* __restrict__ src_of_slot) {
+#pragma unroll
+    for (int s = 0; s < kKeySteps; ++s) {
+        const int64_t i = p0 + s * kWave + lane;
+        const bool in = i < wend;
+        const bool valid = in && valid_id(key[s], E);
+        const uint64_t peers = match_peers(valid ? key[s] : 0, nbits, __ballot(valid));
+        int32_t first = 0;
+        if (valid) first = wrun[key[s]];
+        if (valid && (peers & lanemask_lt()) == 0) wrun[key[s]] = first + __popcll(peers);
+        if (in) {
+            int32_t slot = -1;
+            if (valid) {
+                const int32_t r = first + __popcll(peers & lanemask_lt());
+                if (cap == 0) {
+                    slot = r;
+                } else if (r < cap) {
+                    slot = key[s] * cap + r;
+                }
+            }
+            slot_of[i] = slot;
+            if (slot >= 0 && slot < R) src_of_slot[slot] = static_cast<int32_t>(i);
+        }
+    }
+}
+
+// Per-wave counts of the wave's whole run.  The first pass's ids are already
+// in `key` (loaded early); later passes (blocks above 16K entries) reload.
+__device__ __forceinline__ void count_run(const int32_t* __restrict__ idx, const Run& r,
+                                          const int32_t (&key)[kKeySteps], uint32_t lane, int E,
+                                          int nbits, int32_t* wrun) {
+    count_pass(key, r.wbegin, r.wend, lane, E, nbits, wrun);
+    for (int p = 1; p < r.passes; ++p) {
+        int32_t k2[kKeySteps];
+        const int64_t p0 = r.wbegin + static_cast<int64_t>(p) * kKeySteps * kWave;
+        load_pass(idx, p0, r.wend, lane, k2);
+        count_pass(k2, p0, r.wend, lane, E, nbits, wrun);
+    }
+}
+
+// Everything after total, prior and num_invalid are in LDS and every ranking
+// wave has counted its run (all threads call it, after a barrier).
+__device__ void finish_layout(const int32_t* __restrict__ idx, int64_t n, int E, int cap,
+                              int nblocks, int64_t R, const RankLds& l, const Run& r,
+                              const int32_t (&key)[kKeySteps], int32_t num_invalid,
+                              int32_t* s_dropped, int32_t* __restrict__ count,
                               int32_t* __restrict__ offset, int32_t* __restrict__ slot_of,
                               int32_t* __restrict__ src_of_slot, int32_t* __restrict__ status) {
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const uint32_t lane = lane_id();
+    const int rw = rank_waves(E);
+    const int rs = E + 1;  // row stride of l.run
 
     // Exclusive scan of total into off (wave 0; each lane owns a run of
     // consecutive experts), and the number of entries dropped by the capacity.
@@ -177,16 +233,17 @@ __device__ void finish_layout(const int32_t* __restrict__ idx, const int32_t* st
             run_sum += l.total[e];
         }
         if (lane == kWave - 1) l.off[E] = incl;
-        const int32_t drop_all = wave_inclusive_scan(drop);
-        if (lane == kWave - 1) *s_dropped = drop_all;
+        if (cap > 0) {
+            const int32_t drop_all = wave_inclusive_scan(drop);
+            if (lane == kWave - 1) *s_dropped = drop_all;
+        } else if (lane == 0) {
+            *s_dropped = 0;
+        }
     }
-    const int rw = rank_waves(E);
-    const int rs = E + 1;  // row stride of l.run
-    for (int e = tid; e < rw * rs; e += blockDim.x) l.run[e] = 0;
     __syncthreads();
 
     if (b == 0) {
-        for (int e = tid; e < E; e += blockDim.x) {
+        for (int e = tid; e < E; e += kRankThreads) {
             count[e] = l.total[e];
             offset[e] = l.off[e];
         }
@@ -197,34 +254,13 @@ __device__ void finish_layout(const int32_t* __restrict__ idx, const int32_t* st
         }
     }
 
-    // Per-wave histograms of this block's entries.  Ranking wave w owns the
-    // contiguous run [begin + w*S, begin + (w+1)*S), S a multiple of 64;
-    // runs past the end of the block are empty.
-    const int nbits = key_bits(E);
-    const int64_t begin = static_cast<int64_t>(b) * chunk;
-    const int64_t end = (begin + chunk < n) ? begin + chunk : n;
-    const int S = ((chunk / rw + kWave - 1) / kWave) * kWave;
-    const int64_t wbegin = begin + static_cast<int64_t>(wave) * S;
-    int32_t* wrun = l.run + wave * rs;
-    if (wave < rw) {
-        for (int step = 0; step < S; step += kWave) {
-            const int64_t i = wbegin + step + lane;
-            const bool in = i < end;
-            const int32_t key = !in ? -1 : (stage ? stage[i - begin] : idx[i]);
-            const bool valid = in && valid_id(key, E);
-            const uint64_t peers = match_peers(valid ? key : 0, nbits, __ballot(valid));
-            if (valid && (peers & lanemask_lt()) == 0) wrun[key] += __popcll(peers);
-        }
-    }
-    __syncthreads();
-
     // First rank of each (wave, expert): entries in earlier blocks, then in
     // earlier waves of this block.  For the contiguous layout the expert's
     // offset is folded in, so the value is directly a receive row; for the
     // fixed-capacity layout it stays the rank inside the expert.  Each
     // 16-lane row takes one expert, lane w holding wave w's count, and an
     // exclusive row scan gives every wave its start (rw <= 16).
-    for (int e0 = 0; e0 < E; e0 += static_cast<int>(blockDim.x) / 16) {
+    for (int e0 = 0; e0 < E; e0 += kRankThreads / 16) {
         const int e = e0 + tid / 16;
         const int w = tid & 15;
         const bool mine = e < E && w < rw;
@@ -236,47 +272,33 @@ __device__ void finish_layout(const int32_t* __restrict__ idx, const int32_t* st
 
     // Rank pass in (t, j) order: lane rank among same-expert lanes below it.
     if (wave < rw) {
-        for (int step = 0; step < S; step += kWave) {
-            const int64_t i = wbegin + step + lane;
-            const bool in = i < end;
-            const int32_t key = !in ? -1 : (stage ? stage[i - begin] : idx[i]);
-            const bool valid = in && valid_id(key, E);
-            const uint64_t peers = match_peers(valid ? key : 0, nbits, __ballot(valid));
-            int32_t first = 0;
-            if (valid) first = wrun[key];
-            if (valid && (peers & lanemask_lt()) == 0) wrun[key] = first + __popcll(peers);
-            if (in) {
-                int32_t slot = -1;
-                if (valid) {
-                    const int32_t r = first + __popcll(peers & lanemask_lt());
-                    if (cap == 0) {
-                        slot = r;
-                    } else if (r < cap) {
-                        slot = key * cap + r;
-                    }
-                }
-                slot_of[i] = slot;
-                if (slot >= 0 && slot < R) src_of_slot[slot] = static_cast<int32_t>(i);
-            }
+        const int nbits = key_bits(E);
+        int32_t* wrun = l.run + wave * rs;
+        rank_pass(key, r.wbegin, r.wend, lane, E, cap, nbits, R, wrun, slot_of, src_of_slot);
+        for (int p = 1; p < r.passes; ++p) {
+            int32_t k2[kKeySteps];
+            const int64_t p0 = r.wbegin + static_cast<int64_t>(p) * kKeySteps * kWave;
+            load_pass(idx, p0, r.wend, lane, k2);
+            rank_pass(k2, p0, r.wend, lane, E, cap, nbits, R, wrun, slot_of, src_of_slot);
         }
     }
 
     // Receive rows that no entry fills get src_of_slot = -1.
     if (cap == 0) {
-        const int64_t gtid = static_cast<int64_t>(b) * blockDim.x + tid;
-        const int64_t gstride = static_cast<int64_t>(nblocks) * blockDim.x;
-        for (int64_t r = l.off[E] + gtid; r < R; r += gstride) src_of_slot[r] = -1;
+        const int64_t gtid = static_cast<int64_t>(b) * kRankThreads + tid;
+        const int64_t gstride = static_cast<int64_t>(nblocks) * kRankThreads;
+        for (int64_t row = l.off[E] + gtid; row < R; row += gstride) src_of_slot[row] = -1;
     } else {
         for (int e = b; e < E; e += nblocks) {
             int32_t* rows = src_of_slot + static_cast<int64_t>(e) * cap;
-            for (int r = min(l.total[e], cap) + tid; r < cap; r += blockDim.x) rows[r] = -1;
+            for (int rr = min(l.total[e], cap) + tid; rr < cap; rr += kRankThreads) rows[rr] = -1;
         }
     }
 }
 
 // ---- single-pass path --------------------------------------------------------
 
-__global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(
+__global__ __launch_bounds__(kRankThreads) void layout_single_kernel(
         const int32_t* __restrict__ idx, int64_t n, int E, int cap, int chunk, int nblocks,
         int64_t R, int32_t* __restrict__ count, int32_t* __restrict__ offset,
         int32_t* __restrict__ slot_of, int32_t* __restrict__ src_of_slot,
@@ -285,10 +307,22 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(
     __shared__ int32_t s_invalid, s_dropped;
     const RankLds l = carve(sm, E);
     const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += kSingleThreads) {
+    const int wave = tid / kWave;
+    const uint32_t lane = lane_id();
+    const int rw = rank_waves(E);
+    const int64_t begin = static_cast<int64_t>(blockIdx.x) * chunk;
+    const int64_t end = (begin + chunk < n) ? begin + chunk : n;
+    const Run r = wave_run(begin, end, chunk, rw, wave);
+    int32_t key[kKeySteps];
+    load_pass(idx, r.wbegin, r.wend, lane, key);
+
+    for (int e = tid; e < E; e += kRankThreads) {
         l.total[e] = 0;
         l.prior[e] = 0;
     }
+    int32_t* wrun = l.run + wave * (E + 1);
+    if (wave < rw)
+        for (int e = lane; e <= E; e += kWave) wrun[e] = 0;
     if (tid == 0) s_invalid = 0;
     __syncthreads();
 
@@ -297,15 +331,14 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(
     // flight per pass (idx is 16-byte aligned; the last, partial group is read
     // entry by entry).
     constexpr int kGroups = 8;
-    const int64_t begin = static_cast<int64_t>(blockIdx.x) * chunk;
     const int64_t ngroups = (n + 3) / 4;
     const int4* idx4 = reinterpret_cast<const int4*>(idx);
     int32_t invalid = 0;
-    for (int64_t g0 = 0; g0 < ngroups; g0 += kGroups * kSingleThreads) {
+    for (int64_t g0 = 0; g0 < ngroups; g0 += kGroups * kRankThreads) {
         int4 q[kGroups];
 #pragma unroll
         for (int u = 0; u < kGroups; ++u) {
-            const int64_t g = g0 + u * kSingleThreads + tid;
+            const int64_t g = g0 + u * kRankThreads + tid;
             if (4 * g + 3 < n) {
                 q[u] = idx4[g];
             } else {
@@ -317,13 +350,13 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(
         }
 #pragma unroll
         for (int u = 0; u < kGroups; ++u) {
-            const int64_t i0 = 4 * (g0 + u * kSingleThreads + tid);
-            const int32_t key[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+            const int64_t i0 = 4 * (g0 + u * kRankThreads + tid);
+            const int32_t k4[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                if (valid_id(key[c], E)) {
-                    atomicAdd(&l.total[key[c]], 1);
-                    if (i0 + c < begin) atomicAdd(&l.prior[key[c]], 1);
+                if (valid_id(k4[c], E)) {
+                    atomicAdd(&l.total[k4[c]], 1);
+                    if (i0 + c < begin) atomicAdd(&l.prior[k4[c]], 1);
                 } else if (i0 + c < n) {
                     ++invalid;
                 }
@@ -331,23 +364,29 @@ __global__ __launch_bounds__(kSingleThreads) void layout_single_kernel(
         }
     }
     if (invalid) atomicAdd(&s_invalid, invalid);
-    int32_t* stage = chunk <= kStageMax ? sm + rank_lds_words(E) : nullptr;
-    if (stage) {
-        const int64_t end = (begin + chunk < n) ? begin + chunk : n;
-        stage_keys(idx, begin, end, chunk, stage);
-    }
+    if (wave < rw) count_run(idx, r, key, lane, E, key_bits(E), wrun);
     __syncthreads();
 
-    finish_layout(idx, stage, n, E, cap, chunk, nblocks, R, l, s_invalid, &s_dropped, count,
-                  offset, slot_of, src_of_slot, status);
+    finish_layout(idx, n, E, cap, nblocks, R, l, r, key, s_invalid, &s_dropped, count, offset,
+                  slot_of, src_of_slot, status);
 }
 
 // ---- two-pass path -----------------------------------------------------------
 
-// Column-major block-histogram table: column e (e = E counts invalid ids)
-// holds one count per block, padded with zeros to kTwoPassMaxBlocks, so a
-// column is 16 groups of 16 bytes: one DPP row of 16 lanes.
-constexpr int kTableStride = kTwoPassMaxBlocks;
+// Reads 16-byte groups of routing entries [i0, i0+4) (entries at or past
+// `end` read as -1).  idx is 16-byte aligned.
+__device__ __forceinline__ int4 load_group(const int32_t* __restrict__ idx, int64_t i0, int64_t end) {
+    int4 q;
+    if (i0 + 3 < end) {
+        q = *reinterpret_cast<const int4*>(idx + i0);
+    } else {
+        q.x = (i0 + 0 < end) ? idx[i0 + 0] : -1;
+        q.y = (i0 + 1 < end) ? idx[i0 + 1] : -1;
+        q.z = (i0 + 2 < end) ? idx[i0 + 2] : -1;
+        q.w = -1;
+    }
+    return q;
+}
 
 __global__ __launch_bounds__(kHistThreads) void layout_hist_kernel(
         const int32_t* __restrict__ idx, int64_t n, int E, int chunk, int nblocks,
@@ -390,7 +429,7 @@ __global__ __launch_bounds__(kHistThreads) void layout_hist_kernel(
     }
 }
 
-__global__ __launch_bounds__(1024) void layout_rank_kernel(
+__global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
         const int32_t* __restrict__ idx, int64_t n, int E, int cap, int chunk, int nblocks,
         int64_t R, const int32_t* __restrict__ block_hist, int32_t* __restrict__ count,
         int32_t* __restrict__ offset, int32_t* __restrict__ slot_of,
@@ -400,32 +439,25 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
     const RankLds l = carve(sm, E);
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const uint32_t lane = lane_id();
+    const int rw = rank_waves(E);
     const int64_t begin = static_cast<int64_t>(b) * chunk;
     const int64_t end = (begin + chunk < n) ? begin + chunk : n;
-    int32_t* stage = chunk <= kStageMax ? sm + rank_lds_words(E) : nullptr;
+    const Run r = wave_run(begin, end, chunk, rw, wave);
 
-    // Every global load of the prologue is issued before any is used, so the
-    // prologue costs one memory latency: this block's entries (at most four
-    // 16-byte groups per thread) and the whole table.  The table is read as
-    // 1 KiB per wave instruction: 16 lanes (a DPP row) cover one column, 4
-    // columns per instruction, and a row reduction gives the column's total
-    // and its part before this block.
+    // Every global load of the prologue is issued before any is used: first
+    // this wave's run of ids, then the whole table, read as 1 KiB per wave
+    // instruction with 16 lanes (a DPP row) per column and 4 columns per
+    // instruction.
+    int32_t key[kKeySteps];
+    load_pass(idx, r.wbegin, r.wend, lane, key);
     constexpr int kColsPerLoad = kWave / 16;
-    const int ng = stage ? chunk / 4 : 0;
+    constexpr int kColsPerRound = kColsPerLoad * (kRankThreads / kWave);
+    constexpr int kMaxLoads = (kMaxExperts + 1 + kColsPerRound - 1) / kColsPerRound;
     const int ncols = E + 1;
-    const int loads_per_wave =
-        (ncols + kColsPerLoad * (kRankThreads / kWave) - 1) / (kColsPerLoad * (kRankThreads / kWave));
-    int4 keys[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int g = u * kRankThreads + tid;
-        if (g < ng) keys[u] = load_group(idx, begin + 4 * g, end);
-    }
-    constexpr int kMaxLoads = (kMaxExperts + 1 + kColsPerLoad * (kRankThreads / kWave) - 1) /
-                              (kColsPerLoad * (kRankThreads / kWave));
-    const int wave = tid / kWave;
-    const int lane = tid & (kWave - 1);
-    const int grp = lane & 15;                       // 16-byte group inside the column
+    const int loads_per_wave = (ncols + kColsPerRound - 1) / kColsPerRound;
+    const int grp = lane & 15;  // 16-byte group inside the column
     int4 q[kMaxLoads];
 #pragma unroll
     for (int m = 0; m < kMaxLoads; ++m) {
@@ -436,11 +468,14 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
             q[m] = make_int4(0, 0, 0, 0);
     }
 
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int g = u * kRankThreads + tid;
-        if (g < ng) reinterpret_cast<int4*>(stage)[g] = keys[u];
+    // This wave's counts, built while the table loads are in flight.
+    int32_t* wrun = l.run + wave * (E + 1);
+    if (wave < rw) {
+        for (int e = lane; e <= E; e += kWave) wrun[e] = 0;
+        count_run(idx, r, key, lane, E, key_bits(E), wrun);
     }
+
+    // Column totals and the part of each column before this block.
 #pragma unroll
     for (int m = 0; m < kMaxLoads; ++m) {
         if (m < loads_per_wave) {  // uniform across the wave
@@ -466,8 +501,8 @@ __global__ __launch_bounds__(1024) void layout_rank_kernel(
     }
     __syncthreads();
 
-    finish_layout(idx, stage, n, E, cap, chunk, nblocks, R, l, s_invalid, &s_dropped, count,
-                  offset, slot_of, src_of_slot, status);
+    finish_layout(idx, n, E, cap, nblocks, R, l, r, key, s_invalid, &s_dropped, count, offset,
+                  slot_of, src_of_slot, status);
 }
 
 }  // namespace
@@ -477,14 +512,12 @@ LayoutGeometry layout_geometry(const ep_problem& p) {
     g.entries = static_cast<int64_t>(p.num_tokens) * p.num_topk;
     g.single_pass = g.entries <= kSinglePassMaxEntries;
     // Up to 64 workgroups (single pass: each pays for the whole-table
-    // histogram; two passes: each reads a 64-entry column per expert).
-    // Chunks are multiples of 256 entries (16-byte groups of the histogram
-    // kernel, whole 64-entry ranking steps).
-    const int64_t target_blocks = kTwoPassMaxBlocks;
-    const int64_t min_chunk = 256;
-    int64_t chunk = (g.entries + target_blocks - 1) / target_blocks;
-    if (chunk < min_chunk) chunk = min_chunk;
+    // histogram; two passes: the table has 64 rows per column).  Chunks are
+    // multiples of 256 entries (16-byte groups of the histogram kernel, whole
+    // 64-entry ranking steps).
+    int64_t chunk = (g.entries + kTwoPassMaxBlocks - 1) / kTwoPassMaxBlocks;
     chunk = ((chunk + 255) / 256) * 256;
+    if (chunk < 256) chunk = 256;
     g.chunk = static_cast<int32_t>(chunk);
     const int64_t blocks = (g.entries + chunk - 1) / chunk;
     g.blocks = static_cast<int32_t>(blocks < 1 ? 1 : blocks);
@@ -505,19 +538,19 @@ hipError_t launch_layout(const ep_problem& p, const int32_t* topk_idx, const ep_
     const int E = p.num_experts;
     const int64_t R = (p.capacity == 0) ? g.entries : static_cast<int64_t>(E) * p.capacity;
     if (g.single_pass) {
-        hipLaunchKernelGGL(layout_single_kernel, dim3(g.blocks), dim3(kSingleThreads),
-                           rank_lds_bytes(E, g.chunk), stream, topk_idx, g.entries, E,
-                           p.capacity, g.chunk, g.blocks, R, out.count, out.offset, out.slot_of,
+        hipLaunchKernelGGL(layout_single_kernel, dim3(g.blocks), dim3(kRankThreads),
+                           rank_lds_bytes(E), stream, topk_idx, g.entries, E, p.capacity,
+                           g.chunk, g.blocks, R, out.count, out.offset, out.slot_of,
                            out.src_of_slot, out.status);
         return hipGetLastError();
     }
     const size_t lds_hist = static_cast<size_t>(E + 1) * 4;
     hipLaunchKernelGGL(layout_hist_kernel, dim3(g.blocks), dim3(kHistThreads), lds_hist, stream,
                        topk_idx, g.entries, E, g.chunk, g.blocks, block_hist);
-    hipLaunchKernelGGL(layout_rank_kernel, dim3(g.blocks), dim3(kRankThreads),
-                       rank_lds_bytes(E, g.chunk), stream, topk_idx, g.entries, E, p.capacity, g.chunk,
-                       g.blocks, R, block_hist, out.count, out.offset, out.slot_of,
-                       out.src_of_slot, out.status);
+    hipLaunchKernelGGL(layout_rank_kernel, dim3(g.blocks), dim3(kRankThreads), rank_lds_bytes(E),
+                       stream, topk_idx, g.entries, E, p.capacity, g.chunk, g.blocks, R,
+                       block_hist, out.count, out.offset, out.slot_of, out.src_of_slot,
+                       out.status);
     return hipGetLastError();
 }
 
