@@ -148,6 +148,7 @@ __device__ __forceinline__ void count_pass(const int32_t (&key)[kKeySteps], int6
                                            int32_t* wrun) {
 #pragma unroll
     for (int s = 0; s < kKeySteps; ++s) {
+        if (p0 + s * kWave >= wend) break;  // uniform: past the end of the run
         const int64_t i = p0 + s * kWave + lane;
         const bool valid = i < wend && valid_id(key[s], E);
         const uint64_t peers = match_peers(valid ? key[s] : 0, nbits, __ballot(valid));
@@ -163,6 +164,7 @@ __device__ __forceinline__ void rank_pass(const int32_t (&key)[kKeySteps], int64
                                           int32_t* __restrict__ src_of_slot) {
 #pragma unroll
     for (int s = 0; s < kKeySteps; ++s) {
+        if (p0 + s * kWave >= wend) break;  // uniform: past the end of the run
         const int64_t i = p0 + s * kWave + lane;
         const bool in = i < wend;
         const bool valid = in && valid_id(key[s], E);
