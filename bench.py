@@ -160,6 +160,8 @@ def main():
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--path", choices=["separate", "fused"], default="separate",
+                    help="separate: ep_layout then ep_dispatch; fused: ep_layout_dispatch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run one device-to-device copy of 256 MiB (for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -201,8 +203,14 @@ def main():
     ws = ep.alloc_workspace(prob, dev)
     recv_x, recv_s = ep.alloc_recv(prob, dev)
     y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
-    do_layout = ep.prepare_layout(prob, idx, lay, ws)
-    do_dispatch = ep.prepare_dispatch(prob, x, lay, recv_x, recv_s)
+    fused = args.path == "fused"
+    if fused:
+        # one call does both; the layout bracket below is left empty
+        do_layout = lambda s: None  # noqa: E731
+        do_dispatch = ep.prepare_layout_dispatch(prob, idx, lay, ws, x, recv_x, recv_s)
+    else:
+        do_layout = ep.prepare_layout(prob, idx, lay, ws)
+        do_dispatch = ep.prepare_dispatch(prob, x, lay, recv_x, recv_s)
     do_combine = ep.prepare_combine(prob, eo, lay, w, y)
     stream = torch.cuda.current_stream()
 
@@ -257,11 +265,14 @@ def main():
     total_bytes = nb["dispatch_total"] + nb["combine_total"]
     value = total_bytes / (ms_per_step / 1e3) / 1e9
 
-    kernels = {
-        "dispatch_bf16_kernel" if not wl.fp8 else "dispatch_fp8_kernel":
-            (dispatch_ms, nb["dispatch_kernel"], "ep_dispatch.hip"),
-        "combine_kernel": (combine_ms, nb["combine_kernel"], "ep_combine.hip"),
-    }
+    if fused:
+        disp_entry = ("layout_dispatch_kernel",
+                      (dispatch_ms, nb["dispatch_kernel"] + nb["layout_kernels"], "ep_fused.hip"))
+    else:
+        disp_entry = ("dispatch_bf16_kernel" if not wl.fp8 else "dispatch_fp8_kernel",
+                      (dispatch_ms, nb["dispatch_kernel"], "ep_dispatch.hip"))
+    kernels = {disp_entry[0]: disp_entry[1],
+               "combine_kernel": (combine_ms, nb["combine_kernel"], "ep_combine.hip")}
     dom = max(kernels, key=lambda n: kernels[n][0])
     dom_ms, dom_bytes, dom_src = kernels[dom]
     achieved = dom_bytes / (dom_ms / 1e3) / 1e9
@@ -289,7 +300,9 @@ def main():
                                3: "group-limited 8x32 top-4 groups",
                                4: "Zipf 1.2 without replacement",
                                5: "group-limited + 16 hot experts at 1.5x"}[wl.cid],
-                   "parallelism": "single GPU, all experts local"},
+                   "parallelism": "single GPU, all experts local",
+                   "path": "ep_layout_dispatch + ep_combine" if fused
+                           else "ep_layout + ep_dispatch + ep_combine"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -11,6 +11,8 @@ Entry points (same names as the C ABI):
   ep_layout_workspace_bytes(prob)            -> bytes
   ep_layout(prob, topk_idx, layout, workspace, stream=None)
   ep_dispatch(prob, x, layout, recv_x, recv_scales=None, stream=None)
+  ep_layout_dispatch(prob, topk_idx, layout, workspace, x, recv_x, recv_scales=None,
+                     stream=None)
   ep_combine(prob, expert_out, layout, topk_weights, y, stream=None)
   ep_e4m3_encode(inp, out, stream=None)
   ep_strerror(code)
@@ -29,7 +31,8 @@ __all__ = [
     "Problem", "Layout", "EpError", "ep_num_recv_rows", "ep_layout_workspace_bytes",
     "ep_layout", "ep_dispatch", "ep_combine", "ep_e4m3_encode", "ep_strerror",
     "alloc_workspace", "alloc_recv", "library_path", "load_library",
-    "prepare_layout", "prepare_dispatch", "prepare_combine",
+    "prepare_layout", "prepare_dispatch", "prepare_combine", "ep_layout_dispatch",
+    "prepare_layout_dispatch",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -92,6 +95,8 @@ def load_library():
     lib.ep_layout.argtypes = [P, vp, L, vp, ctypes.c_size_t, vp]
     lib.ep_dispatch.restype = ctypes.c_int
     lib.ep_dispatch.argtypes = [P, vp, L, vp, vp, vp]
+    lib.ep_layout_dispatch.restype = ctypes.c_int
+    lib.ep_layout_dispatch.argtypes = [P, vp, L, vp, ctypes.c_size_t, vp, vp, vp, vp]
     lib.ep_combine.restype = ctypes.c_int
     lib.ep_combine.argtypes = [P, vp, L, vp, vp, vp]
     lib.ep_e4m3_encode.restype = ctypes.c_int
@@ -234,6 +239,31 @@ def ep_dispatch(prob, x, layout, recv_x, recv_scales=None, stream=None):
                                           _stream_handle(stream)))
 
 
+def _layout_dispatch_args(prob, topk_idx, layout, workspace, x, recv_x, recv_scales):
+    torch = _torch()
+    T, H = prob.num_tokens, prob.hidden
+    R = ep_num_recv_rows(prob)
+    idx = _ptr(topk_idx, "topk_idx", torch.int32, T * prob.num_topk, allow_none=True)
+    xp = _ptr(x, "x", torch.bfloat16, T * H, allow_none=True)
+    s = layout._struct(prob)
+    ws = _ptr(workspace, "workspace", allow_none=True)
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if prob.use_fp8:
+        rp = _ptr(recv_x, "recv_x", (torch.uint8, torch.float8_e4m3fn), R * H, allow_none=True)
+        sp = _ptr(recv_scales, "recv_scales", torch.float32, R * (H // 128), allow_none=True)
+    else:
+        rp = _ptr(recv_x, "recv_x", torch.bfloat16, R * H, allow_none=True)
+        sp = None
+    return s, (ctypes.byref(prob), idx, ctypes.byref(s), ws, nbytes, xp, rp, sp)
+
+
+def ep_layout_dispatch(prob, topk_idx, layout, workspace, x, recv_x, recv_scales=None,
+                       stream=None):
+    lib = load_library()
+    _s, args = _layout_dispatch_args(prob, topk_idx, layout, workspace, x, recv_x, recv_scales)
+    _check("ep_layout_dispatch", lib.ep_layout_dispatch(*args, _stream_handle(stream)))
+
+
 def ep_combine(prob, expert_out, layout, topk_weights, y, stream=None):
     torch = _torch()
     lib = load_library()
@@ -307,3 +337,10 @@ def prepare_combine(prob, expert_out, layout, topk_weights, y):
     args = (ctypes.byref(prob), ep, ctypes.byref(s), wp, yp)
     return _Prepared("ep_combine", lib.ep_combine, args,
                      (prob, s, expert_out, layout, topk_weights, y))
+
+
+def prepare_layout_dispatch(prob, topk_idx, layout, workspace, x, recv_x, recv_scales=None):
+    lib = load_library()
+    s, args = _layout_dispatch_args(prob, topk_idx, layout, workspace, x, recv_x, recv_scales)
+    return _Prepared("ep_layout_dispatch", lib.ep_layout_dispatch, args,
+                     (prob, s, topk_idx, layout, workspace, x, recv_x, recv_scales))

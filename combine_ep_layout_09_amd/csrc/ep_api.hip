@@ -100,6 +100,31 @@ int ep_dispatch(const ep_problem* prob, const void* x, const ep_layout_t* layout
                                         static_cast<hipStream_t>(stream)));
 }
 
+int ep_layout_dispatch(const ep_problem* prob, const int32_t* topk_idx, const ep_layout_t* out,
+                       void* workspace, size_t workspace_bytes, const void* x, void* recv_x,
+                       float* recv_scales, void* stream) {
+    int rc = check_problem(prob);
+    if (rc != EP_OK) return rc;
+    rc = check_layout_ptrs(*prob, out, true);
+    if (rc != EP_OK) return rc;
+    if (static_cast<int64_t>(prob->num_tokens) * prob->num_topk > 0 && topk_idx == nullptr)
+        return EP_ERR_ARG;
+    if (!aligned16(topk_idx)) return EP_ERR_ALIGN;
+    if (workspace == nullptr ||
+        static_cast<int64_t>(workspace_bytes) < ep::layout_workspace_bytes(*prob))
+        return EP_ERR_ARG;
+    if (!aligned16(workspace)) return EP_ERR_ALIGN;
+    if (prob->num_tokens > 0) {
+        if (x == nullptr || recv_x == nullptr) return EP_ERR_ARG;
+        if (prob->use_fp8 && recv_scales == nullptr) return EP_ERR_ARG;
+    }
+    if (!aligned16(x) || !aligned16(recv_x) || (prob->use_fp8 && !aligned16(recv_scales)))
+        return EP_ERR_ALIGN;
+    return from_hip(ep::launch_layout_dispatch(*prob, topk_idx, *out, workspace, x, recv_x,
+                                               prob->use_fp8 ? recv_scales : nullptr,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 int ep_combine(const ep_problem* prob, const void* expert_out, const ep_layout_t* layout,
                const float* topk_weights, void* y, void* stream) {
     int rc = check_problem(prob);

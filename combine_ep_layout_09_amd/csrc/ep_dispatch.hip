@@ -29,14 +29,13 @@
 // scales of the tile are collected in LDS and written as one contiguous run
 // per slot.
 
-#include "ep_device.h"
+#include "ep_dispatch_dev.h"
 #include "ep_internal.h"
 
 namespace ep {
 namespace {
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+using namespace dispatch;
 
 constexpr int kMaxThreads = 1024;
 
@@ -44,107 +43,24 @@ template <int VPL>
 __global__ __launch_bounds__(kMaxThreads) void dispatch_bf16_kernel(
         const u32x4* __restrict__ x, int nvec, int k, const int32_t* __restrict__ slot_of,
         int64_t R, u32x4* __restrict__ recv) {
-    const int t = blockIdx.x;
-    const int32_t* slots = slot_of + static_cast<int64_t>(t) * k;
-    const u32x4* row = x + static_cast<int64_t>(t) * nvec;
-    const int base = blockIdx.y * blockDim.x * VPL + threadIdx.x;
-    int v[VPL];
-    u32x4 buf[VPL];
-#pragma unroll
-    for (int u = 0; u < VPL; ++u) {
-        v[u] = min(base + u * static_cast<int>(blockDim.x), nvec - 1);
-        buf[u] = row[v[u]];
-    }
-    for (int j = 0; j < k; ++j) {
-        const int32_t slot = slots[j];
-        if (slot < 0 || slot >= R) continue;
-        u32x4* dst = recv + static_cast<int64_t>(slot) * nvec;
-#pragma unroll
-        for (int u = 0; u < VPL; ++u) __builtin_nontemporal_store(buf[u], dst + v[u]);
-    }
+    Bf16Tile<VPL> tile;
+    tile.load(x, nvec, blockIdx.x, blockIdx.y, blockDim.x, threadIdx.x);
+    tile.store(slot_of + static_cast<int64_t>(blockIdx.x) * k, k, R, recv, nvec);
 }
 
-// Maximum across the 16 lanes of a DPP row (all lanes get the result).
-__device__ __forceinline__ float row16_max(float m) {
-    m = fmaxf(m, __shfl_xor(m, 1, 16));
-    m = fmaxf(m, __shfl_xor(m, 2, 16));
-    m = fmaxf(m, __shfl_xor(m, 4, 16));
-    m = fmaxf(m, __shfl_xor(m, 8, 16));
-    return m;
-}
-
-__device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, float scale) {
-    const float f[4] = {bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
-    uint32_t packed = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t c = (scale == 0.0f) ? 0u : f32_to_e4m3_rne(f[i] / scale);
-        packed |= c << (8 * i);
-    }
-    return packed;
-}
-
-__device__ __forceinline__ float absmax8(const u32x4& p) {
-    float m = fabsf(bf16_lo(p.x));
-    m = fmaxf(m, fabsf(bf16_hi(p.x)));
-    m = fmaxf(m, fabsf(bf16_lo(p.y)));
-    m = fmaxf(m, fabsf(bf16_hi(p.y)));
-    m = fmaxf(m, fabsf(bf16_lo(p.z)));
-    m = fmaxf(m, fabsf(bf16_hi(p.z)));
-    m = fmaxf(m, fabsf(bf16_lo(p.w)));
-    m = fmaxf(m, fabsf(bf16_hi(p.w)));
-    return m;
-}
-
-// nvec = H / 8 (a multiple of 16); nblk = H / 128.  The workgroup width is a
-// multiple of 64, so 16-lane groups never straddle the end of the row: a group
-// past the end maps as a whole onto the row's last group.
 template <int VPL>
 __global__ __launch_bounds__(kMaxThreads) void dispatch_fp8_kernel(
         const u32x4* __restrict__ x, int nvec, int nblk, int k,
         const int32_t* __restrict__ slot_of, int64_t R, u32x2* __restrict__ recv_q,
         float* __restrict__ recv_scales) {
     extern __shared__ float s_scale[];  // [blockDim * VPL / 16] scales of this tile
-    const int t = blockIdx.x;
-    const int32_t* slots = slot_of + static_cast<int64_t>(t) * k;
-    const u32x4* row = x + static_cast<int64_t>(t) * nvec;
-    const int tile0 = blockIdx.y * blockDim.x * VPL;
-    int v[VPL];
-    u32x4 buf[VPL];
-#pragma unroll
-    for (int u = 0; u < VPL; ++u) {
-        const int vv = tile0 + u * static_cast<int>(blockDim.x) + threadIdx.x;
-        v[u] = (vv < nvec) ? vv : nvec - 16 + (vv & 15);
-        buf[u] = row[v[u]];
-    }
-    u32x2 q[VPL];
-#pragma unroll
-    for (int u = 0; u < VPL; ++u) {
-        const float amax = row16_max(absmax8(buf[u]));
-        const float scale = amax / 448.0f;
-        q[u].x = quant4(buf[u].x, buf[u].y, scale);
-        q[u].y = quant4(buf[u].z, buf[u].w, scale);
-        const int vv = tile0 + u * static_cast<int>(blockDim.x) + threadIdx.x;
-        if ((threadIdx.x & 15) == 0 && vv < nvec) s_scale[(vv - tile0) >> 4] = scale;
-    }
-    for (int j = 0; j < k; ++j) {
-        const int32_t slot = slots[j];
-        if (slot < 0 || slot >= R) continue;
-        u32x2* dst = recv_q + static_cast<int64_t>(slot) * nvec;
-#pragma unroll
-        for (int u = 0; u < VPL; ++u) __builtin_nontemporal_store(q[u], dst + v[u]);
-    }
+    const int32_t* slots = slot_of + static_cast<int64_t>(blockIdx.x) * k;
+    Fp8Tile<VPL> tile;
+    tile.load_quantise(x, nvec, blockIdx.x, blockIdx.y, blockDim.x, threadIdx.x, s_scale);
+    tile.store(slots, k, R, recv_q, nvec);
     __syncthreads();
-    // Scales: this tile covers blocks [tile0/16, tile0/16 + nb) of the row.
-    const int b0 = tile0 >> 4;
-    const int nb = min(static_cast<int>(blockDim.x) * VPL / 16, nblk - b0);
-    for (int i = threadIdx.x; i < k * nb; i += blockDim.x) {
-        const int j = i / nb;
-        const int b = i - j * nb;
-        const int32_t slot = slots[j];
-        if (slot >= 0 && slot < R)
-            recv_scales[static_cast<int64_t>(slot) * nblk + b0 + b] = s_scale[b];
-    }
+    fp8_store_scales(s_scale, slots, k, R, recv_scales, nblk, blockIdx.y, blockDim.x, VPL,
+                     threadIdx.x);
 }
 
 // Elementwise use of the same encoder, for callers that quantise other data.
@@ -182,7 +98,7 @@ DispatchShape dispatch_shape(int nvec, int T) {
     // that enough waves exist to keep HBM busy.
     if (T < 1024) return {1, row_tile_shape(nvec, 1)};
     if (nvec <= 128) return {1, {((nvec + 63) / 64) * 64, 1}};
-    const int vpl = nvec >= 1024 ? 8 : (nvec + 127) / 128;
+    const int vpl = two_wave_vpl(nvec);
     return {vpl, {128, (nvec + 128 * vpl - 1) / (128 * vpl)}};
 }
 

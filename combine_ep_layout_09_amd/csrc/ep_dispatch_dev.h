@@ -1,0 +1,164 @@
+// ep_dispatch_dev.h -- device code of dispatch, shared by the dispatch kernels
+// and the fused layout + dispatch kernel.
+//
+// A "tile" is the part of one token row that one group of lanes (gsize lanes,
+// a multiple of 64) moves: lane gtid owns VPL 16-byte pieces spaced gsize
+// pieces apart, so every wave instruction covers 1 KiB of contiguous memory.
+// Loading (and, for FP8, quantising) is separate from storing, so a caller can
+// issue its row loads before it knows the receive rows.  Lanes past the end of
+// the row redo the last piece (the last 16-lane group for FP8) and store the
+// same bytes to the same place, which keeps the loads free of branches.
+//
+// FP8: a lane holds 8 channels, so a 128-channel block is 16 adjacent lanes
+// (one DPP row).  The block maximum of |x| is reduced across the row, the
+// scale is amax / 448 (IEEE fp32 division), each channel is divided by it
+// (IEEE fp32 division) and encoded with round-to-nearest-even.
+#pragma once
+
+#include "ep_device.h"
+
+namespace ep {
+namespace dispatch {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int VPL>
+struct Bf16Tile {
+    int v[VPL];
+    u32x4 buf[VPL];
+
+    __device__ __forceinline__ void load(const u32x4* __restrict__ x, int nvec, int t, int tile,
+                                         int gsize, int gtid) {
+        const u32x4* row = x + static_cast<int64_t>(t) * nvec;
+        const int base = tile * gsize * VPL + gtid;
+#pragma unroll
+        for (int u = 0; u < VPL; ++u) {
+            v[u] = min(base + u * gsize, nvec - 1);
+            buf[u] = row[v[u]];
+        }
+    }
+
+    // Non-temporal stores to every slot in [0, R); slots[j] is the same for
+    // every lane of the wave.
+    __device__ __forceinline__ void store(const int32_t* slots, int k, int64_t R,
+                                          u32x4* __restrict__ recv, int nvec) const {
+        for (int j = 0; j < k; ++j) {
+            const int32_t slot = __builtin_amdgcn_readfirstlane(slots[j]);
+            if (slot < 0 || slot >= R) continue;
+            u32x4* dst = recv + static_cast<int64_t>(slot) * nvec;
+#pragma unroll
+            for (int u = 0; u < VPL; ++u) __builtin_nontemporal_store(buf[u], dst + v[u]);
+        }
+    }
+};
+
+// Maximum across the 16 lanes of a DPP row (all lanes get the result).
+__device__ __forceinline__ float row16_max(float m) {
+    m = fmaxf(m, __shfl_xor(m, 1, 16));
+    m = fmaxf(m, __shfl_xor(m, 2, 16));
+    m = fmaxf(m, __shfl_xor(m, 4, 16));
+    m = fmaxf(m, __shfl_xor(m, 8, 16));
+    return m;
+}
+
+__device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, float scale) {
+    const float f[4] = {bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t c = (scale == 0.0f) ? 0u : f32_to_e4m3_rne(f[i] / scale);
+        packed |= c << (8 * i);
+    }
+    return packed;
+}
+
+__device__ __forceinline__ float absmax8(const u32x4& p) {
+    float m = fabsf(bf16_lo(p.x));
+    m = fmaxf(m, fabsf(bf16_hi(p.x)));
+    m = fmaxf(m, fabsf(bf16_lo(p.y)));
+    m = fmaxf(m, fabsf(bf16_hi(p.y)));
+    m = fmaxf(m, fabsf(bf16_lo(p.z)));
+    m = fmaxf(m, fabsf(bf16_hi(p.z)));
+    m = fmaxf(m, fabsf(bf16_lo(p.w)));
+    m = fmaxf(m, fabsf(bf16_hi(p.w)));
+    return m;
+}
+
+// nvec = H / 8 (a multiple of 16).  gsize is a multiple of 64, so 16-lane
+// groups never straddle the end of the row: a group past the end maps as a
+// whole onto the row's last group.
+template <int VPL>
+struct Fp8Tile {
+    int v[VPL];
+    u32x2 q[VPL];
+    u32x4 buf[VPL];  // raw bf16 pieces between load() and quantise()
+
+    __device__ __forceinline__ void load(const u32x4* __restrict__ x, int nvec, int t, int tile,
+                                         int gsize, int gtid) {
+        const u32x4* row = x + static_cast<int64_t>(t) * nvec;
+        const int tile0 = tile * gsize * VPL;
+#pragma unroll
+        for (int u = 0; u < VPL; ++u) {
+            const int vv = tile0 + u * gsize + gtid;
+            v[u] = (vv < nvec) ? vv : nvec - 16 + (vv & 15);
+            buf[u] = row[v[u]];
+        }
+    }
+
+    // s_scale: this tile's gsize * VPL / 16 block scales (LDS).
+    __device__ __forceinline__ void quantise(int nvec, int tile, int gsize, int gtid,
+                                             float* s_scale) {
+        const int tile0 = tile * gsize * VPL;
+#pragma unroll
+        for (int u = 0; u < VPL; ++u) {
+            const float amax = row16_max(absmax8(buf[u]));
+            const float scale = amax / 448.0f;
+            q[u].x = quant4(buf[u].x, buf[u].y, scale);
+            q[u].y = quant4(buf[u].z, buf[u].w, scale);
+            const int vv = tile0 + u * gsize + gtid;
+            if ((gtid & 15) == 0 && vv < nvec) s_scale[(vv - tile0) >> 4] = scale;
+        }
+    }
+
+    __device__ __forceinline__ void load_quantise(const u32x4* __restrict__ x, int nvec, int t,
+                                                  int tile, int gsize, int gtid, float* s_scale) {
+        load(x, nvec, t, tile, gsize, gtid);
+        quantise(nvec, tile, gsize, gtid, s_scale);
+    }
+
+    __device__ __forceinline__ void store(const int32_t* slots, int k, int64_t R,
+                                          u32x2* __restrict__ recv_q, int nvec) const {
+        for (int j = 0; j < k; ++j) {
+            const int32_t slot = __builtin_amdgcn_readfirstlane(slots[j]);
+            if (slot < 0 || slot >= R) continue;
+            u32x2* dst = recv_q + static_cast<int64_t>(slot) * nvec;
+#pragma unroll
+            for (int u = 0; u < VPL; ++u) __builtin_nontemporal_store(q[u], dst + v[u]);
+        }
+    }
+};
+
+// Writes the tile's block scales (staged in s_scale by load_quantise, after a
+// barrier) as one contiguous run per slot.
+__device__ __forceinline__ void fp8_store_scales(const float* s_scale, const int32_t* slots, int k,
+                                                 int64_t R, float* __restrict__ recv_scales,
+                                                 int nblk, int tile, int gsize, int vpl, int gtid) {
+    const int b0 = (tile * gsize * vpl) >> 4;
+    const int nb = min(gsize * vpl / 16, nblk - b0);
+    for (int i = gtid; i < k * nb; i += gsize) {
+        const int j = i / nb;
+        const int b = i - j * nb;
+        const int32_t slot = slots[j];
+        if (slot >= 0 && slot < R)
+            recv_scales[static_cast<int64_t>(slot) * nblk + b0 + b] = s_scale[b];
+    }
+}
+
+// Pieces per lane for two-wave tiles covering whole rows of up to 1024 pieces.
+__host__ __device__ constexpr int two_wave_vpl(int nvec) {
+    return nvec >= 1024 ? 8 : (nvec + 127) / 128;
+}
+
+}  // namespace dispatch
+}  // namespace ep

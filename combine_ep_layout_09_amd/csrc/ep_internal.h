@@ -29,12 +29,20 @@ struct LayoutGeometry {
 };
 
 LayoutGeometry layout_geometry(const ep_problem& p);
+LayoutGeometry layout_geometry_two_pass(const ep_problem& p);
 int64_t layout_workspace_bytes(const ep_problem& p);
 
+// Largest routing table (T*k entries) that ep_layout_dispatch handles in one
+// kernel; larger tables run the layout and dispatch kernels in turn.
+constexpr int kFusedMaxEntries = 8192;
+
 hipError_t launch_layout(const ep_problem& p, const int32_t* topk_idx, const ep_layout_t& out,
-                         int32_t* block_hist, hipStream_t stream);
+                         int32_t* workspace, hipStream_t stream);
 hipError_t launch_dispatch(const ep_problem& p, const void* x, const int32_t* slot_of,
                            void* recv_x, float* recv_scales, hipStream_t stream);
+hipError_t launch_layout_dispatch(const ep_problem& p, const int32_t* topk_idx,
+                                  const ep_layout_t& out, void* workspace, const void* x,
+                                  void* recv_x, float* recv_scales, hipStream_t stream);
 hipError_t launch_combine(const ep_problem& p, const void* expert_out, const int32_t* slot_of,
                           const float* topk_weights, void* y, hipStream_t stream);
 hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);

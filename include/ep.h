@@ -113,10 +113,10 @@ typedef struct ep_layout_t {
 /* R for this problem (T*k or E*cap), or -1 if the problem is invalid. */
 int64_t ep_num_recv_rows(const ep_problem* prob);
 
-/* Bytes of device workspace ep_layout needs for this problem (a multiple of
- * 256; at least 256), or -1 if the problem is invalid.  The workspace holds
- * per-block expert histograms between the layout's two kernels; its contents
- * need no initialisation and are scratch after the call. */
+/* Bytes of device workspace ep_layout and ep_layout_dispatch need for this
+ * problem (a multiple of 256: the block-histogram table of 64 * (E + 1)
+ * int32), or -1 if the problem is invalid.  Its contents need no
+ * initialisation and are scratch after the call. */
 int64_t ep_layout_workspace_bytes(const ep_problem* prob);
 
 /* Routing layout.
@@ -145,6 +145,17 @@ int ep_layout(const ep_problem* prob, const int32_t* topk_idx, const ep_layout_t
  * bit-identical.  x must be finite. */
 int ep_dispatch(const ep_problem* prob, const void* x, const ep_layout_t* layout,
                 void* recv_x, float* recv_scales, void* stream);
+
+/* Layout and dispatch in one call, with the same results as ep_layout
+ * followed by ep_dispatch (every output of both is written).  Arguments as
+ * for ep_layout and ep_dispatch.  For routing tables of up to 8192 entries
+ * (T*k, decode-sized batches) it is one kernel launch in which no workgroup
+ * waits for another: each one derives the slots of its own tokens from the
+ * whole table while its rows load, then stores them; the workspace is not
+ * touched.  Larger tables run the ep_layout and ep_dispatch kernels in turn. */
+int ep_layout_dispatch(const ep_problem* prob, const int32_t* topk_idx, const ep_layout_t* out,
+                       void* workspace, size_t workspace_bytes, const void* x, void* recv_x,
+                       float* recv_scales, void* stream);
 
 /* Combine: y[t][c] = bf16_RNE( fixed-order fused multiply-add chain over
  * j = 0..k-1 with slot_of[t*k+j] >= 0 of topk_weights[t*k+j] *

@@ -24,7 +24,8 @@ def test_library_exports_every_declared_function():
     lib = ep.load_library()
     names = declared_functions()
     assert {"ep_layout", "ep_dispatch", "ep_combine", "ep_num_recv_rows",
-            "ep_layout_workspace_bytes", "ep_strerror", "ep_e4m3_encode"} <= set(names)
+            "ep_layout_workspace_bytes", "ep_strerror", "ep_e4m3_encode",
+            "ep_layout_dispatch"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ep.h but not exported"
 
@@ -78,6 +79,8 @@ def test_bad_problems_rejected_everywhere(prob, code):
     assert lib.ep_layout(ctypes.byref(prob), FAKE, ctypes.byref(s), FAKE, 1 << 30, None) == code
     assert lib.ep_dispatch(ctypes.byref(prob), FAKE, ctypes.byref(s), FAKE, FAKE, None) == code
     assert lib.ep_combine(ctypes.byref(prob), FAKE, ctypes.byref(s), FAKE, FAKE, None) == code
+    assert lib.ep_layout_dispatch(ctypes.byref(prob), FAKE, ctypes.byref(s), FAKE, 1 << 30, FAKE,
+                                  FAKE, FAKE, None) == code
     assert lib.ep_num_recv_rows(ctypes.byref(prob)) == -1
     assert lib.ep_layout_workspace_bytes(ctypes.byref(prob)) == -1
 
@@ -111,6 +114,16 @@ def test_null_and_alignment_checks():
     assert lib.ep_combine(P, FAKE, L, FAKE, None, None) == ep.EP_ERR_ARG
     assert lib.ep_combine(P, FAKE + 4, L, FAKE, FAKE, None) == ep.EP_ERR_ALIGN
     assert lib.ep_combine(P, FAKE, L, FAKE + 2, FAKE, None) == ep.EP_ERR_ALIGN
+    LD = lib.ep_layout_dispatch
+    S = ctypes.byref(_layout_struct())
+    assert LD(P, None, S, FAKE, ws, FAKE, FAKE, None, None) == ep.EP_ERR_ARG
+    assert LD(P, FAKE + 4, S, FAKE, ws, FAKE, FAKE, None, None) == ep.EP_ERR_ALIGN
+    assert LD(P, FAKE, S, FAKE, ws - 1, FAKE, FAKE, None, None) == ep.EP_ERR_ARG
+    assert LD(P, FAKE, S, FAKE, ws, None, FAKE, None, None) == ep.EP_ERR_ARG
+    assert LD(P, FAKE, S, FAKE, ws, FAKE, None, None, None) == ep.EP_ERR_ARG
+    assert LD(P, FAKE, S, FAKE, ws, FAKE + 8, FAKE, None, None) == ep.EP_ERR_ALIGN
+    assert LD(ctypes.byref(p8), FAKE, S, FAKE, ws, FAKE, FAKE, None, None) == ep.EP_ERR_ARG
+    assert LD(P, FAKE, ctypes.byref(_layout_struct(count=None)), FAKE, ws, FAKE, FAKE, None, None) == ep.EP_ERR_ARG
     assert lib.ep_e4m3_encode(None, FAKE, 5, None) == ep.EP_ERR_ARG
     assert lib.ep_e4m3_encode(FAKE, FAKE, -1, None) == ep.EP_ERR_ARG
     assert lib.ep_e4m3_encode(FAKE + 1, FAKE, 5, None) == ep.EP_ERR_ALIGN

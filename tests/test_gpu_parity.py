@@ -55,9 +55,10 @@ class Case:
         self.eo[ref["src_of_slot"] < 0] = NAN_BF16
 
 
-def run_gpu(c, stream=None):
+def run_gpu(c, stream=None, fused=False):
     prob = ep.Problem(c.T, c.H, c.k, c.E, c.cap, c.fp8)
-    print(f"[gpu] {c.name}: {prob!r}", flush=True)
+    print(f"[gpu] {c.name}: {prob!r} {'fused layout+dispatch' if fused else 'separate calls'}",
+          flush=True)
     lay = ep.Layout.empty(prob, DEV)
     for t in (lay.count, lay.offset, lay.slot_of, lay.src_of_slot, lay.status):
         t.fill_(-7)
@@ -76,8 +77,11 @@ def run_gpu(c, stream=None):
     torch.cuda.synchronize()
     ctx = torch.cuda.stream(stream) if stream is not None else torch.cuda.stream(torch.cuda.current_stream())
     with ctx:
-        ep.ep_layout(prob, idx, lay, ws)
-        ep.ep_dispatch(prob, x, lay, recv_x, recv_s)
+        if fused:
+            ep.ep_layout_dispatch(prob, idx, lay, ws, x, recv_x, recv_s)
+        else:
+            ep.ep_layout(prob, idx, lay, ws)
+            ep.ep_dispatch(prob, x, lay, recv_x, recv_s)
         ep.ep_combine(prob, eo, lay, w, y)
     torch.cuda.synchronize()
     out = {n: getattr(lay, n).cpu().numpy() for n in ("count", "offset", "slot_of", "src_of_slot", "status")}
@@ -134,17 +138,19 @@ def check_case(c, got, tokens=None):
 # the five workloads at full size
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
 @pytest.mark.parametrize("cid", [1, 2, 3, 4])
-def test_workload_full(cid):
+def test_workload_full(cid, fused):
     c = Case.from_workload(workloads.make(cid))
-    check_case(c, run_gpu(c))
+    check_case(c, run_gpu(c, fused=fused))
 
 
-def test_workload_large_prefill_sampled():
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+def test_workload_large_prefill_sampled(fused):
     """T=16384, H=7168, E=256, k=8, FP8: full layout check; payload, scales and
     combine checked on sampled tokens (first, last, a ragged spread)."""
     c = Case.from_workload(workloads.make(5), nan_unused=False)
-    got = run_gpu(c)
+    got = run_gpu(c, fused=fused)
     rng = np.random.default_rng(0)
     tokens = np.unique(np.concatenate([[0, 1, c.T - 1], rng.choice(c.T, 509, replace=False)]))
     check_case(c, got, tokens)
@@ -189,15 +195,21 @@ EDGE = [
     dict(T=1025, H=136, k=8, E=64, cap=0, fp8=False, name="layout_two_pass_smallest"),
     dict(T=1171, H=128, k=7, E=1000, cap=0, fp8=False, name="layout_two_pass_many_experts"),
     dict(T=40000, H=128, k=8, E=256, cap=1500, fp8=True, name="layout_two_pass_capacity"),
+    # the largest table the one-kernel layout + dispatch takes (8192 entries),
+    # and few experts (many equal ids, many queries per workgroup)
+    dict(T=1024, H=256, k=8, E=16, cap=0, fp8=False, name="fused_largest_table"),
+    dict(T=2730, H=128, k=3, E=2, cap=3000, fp8=True, name="fused_two_experts_capacity"),
+    dict(T=3, H=8, k=5, E=1000, cap=2, fp8=False, name="fused_few_tokens_many_experts"),
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
 @pytest.mark.parametrize("spec", EDGE, ids=[e["name"] for e in EDGE])
-def test_edge_shapes(spec):
+def test_edge_shapes(spec, fused):
     spec = dict(spec)
     name = spec.pop("name")
     c = _random_case(**spec, seed=zlib.crc32(name.encode()) % 1000, name=name)
-    check_case(c, run_gpu(c))
+    check_case(c, run_gpu(c, fused=fused))
 
 
 def test_duplicate_and_invalid_ids():
@@ -209,9 +221,10 @@ def test_duplicate_and_invalid_ids():
     ids[::13, 3] = E                               # one past the end
     ids[::17, 0] = 1 << 30                         # far out of range
     ids[5] = 3                                     # all k entries to one expert
-    for cap, fp8 in ((0, False), (0, True), (40, True)):
+    for cap, fp8, fused in ((0, False, False), (0, True, False), (40, True, False),
+                            (0, False, True), (40, True, True)):
         c = _random_case(T, 256, k, E, cap, fp8, seed=cap, ids=ids, name=f"dup_invalid_cap{cap}")
-        got = run_gpu(c)
+        got = run_gpu(c, fused=fused)
         check_case(c, got)
         assert got["status"][0] == int(((ids < 0) | (ids >= E)).sum())
 
@@ -249,12 +262,27 @@ def test_fp8_special_rows():
                  name=f"fp8_special_cap{cap}")
         c.nan_unused_rows()
         check_case(c, run_gpu(c))
+        check_case(c, run_gpu(c, fused=True))
 
 
-def test_non_default_stream():
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+def test_non_default_stream(fused):
     c = _random_case(333, 512, 4, 16, 0, True, seed=5, name="side_stream")
     s = torch.cuda.Stream()
-    check_case(c, run_gpu(c, stream=s))
+    check_case(c, run_gpu(c, stream=s, fused=fused))
+
+
+def test_fused_equals_separate_bitwise():
+    """ep_layout_dispatch writes exactly what ep_layout + ep_dispatch write,
+    receive rows and scales included, on the tiny and the decode workloads
+    (one-kernel path) and the skewed workload (two-kernel path)."""
+    for cid in (1, 2, 4):
+        c = Case.from_workload(workloads.make(cid))
+        a = run_gpu(c)
+        b = run_gpu(c, fused=True)
+        for n in a:
+            if a[n] is not None:  # bit patterns: untouched rows hold NaN fill
+                assert np.array_equal(a[n].view(np.uint8), b[n].view(np.uint8)), (cid, n)
 
 
 def test_deterministic_reruns():
