@@ -32,9 +32,11 @@ LayoutGeometry layout_geometry(const ep_problem& p);
 LayoutGeometry layout_geometry_two_pass(const ep_problem& p);
 int64_t layout_workspace_bytes(const ep_problem& p);
 
-// Largest routing table (T*k entries) that ep_layout_dispatch handles in one
-// kernel; larger tables run the layout and dispatch kernels in turn.
+// Small routing tables (T*k entries): ep_layout and ep_layout_dispatch handle
+// them in one kernel in which every workgroup reads the whole table, as long
+// as the id visits of all workgroups together stay below kFusedMaxVisits.
 constexpr int kFusedMaxEntries = 8192;
+constexpr int64_t kFusedMaxVisits = int64_t{1} << 23;
 
 hipError_t launch_layout(const ep_problem& p, const int32_t* topk_idx, const ep_layout_t& out,
                          int32_t* workspace, hipStream_t stream);

@@ -7,25 +7,24 @@
 // stable order inside an expert follows the order-consistency requirement in
 // "[GH-ISSUE #18] Reasons for not calling NVSHMEM public APIs?".
 //
-// The T*k entries (row-major (t, j) order) are split into blocks of `chunk`
-// consecutive entries; each workgroup ranks one block.  Before it can rank, a
-// workgroup needs, per expert, the number of valid entries in the whole table
-// (for the offsets) and in the blocks before its own (for the ranks).
+// Small tables (up to kFusedMaxEntries entries: decode-sized batches): one
+// kernel, in which every workgroup stages the whole routing table in LDS,
+// builds its histogram there, and ranks 64 entries by looking the ids ahead
+// of them up in a per-expert mask of those entries (ep_small_dev.h).  No
+// workgroup waits for another.
 //
-// Single-pass path (tables up to kSinglePassMaxEntries entries: decode-sized
-// batches): one kernel.  Every workgroup reads the whole routing table and
-// builds both histograms itself with LDS atomics; no workgroup waits on
-// another.  LDS atomics cost about one wave instruction per 64 entries per
-// workgroup, which is why this path stops at small tables.
-//
-// Two-pass path (larger tables): layout_hist writes each block's histogram to
+// Larger tables: the T*k entries (row-major (t, j) order) are split into
+// blocks of `chunk` consecutive entries; each workgroup ranks one block.
+// Before it can rank, a workgroup needs, per expert, the number of valid
+// entries in the whole table (for the offsets) and in the blocks before its
+// own (for the ranks).  layout_hist writes each block's histogram to
 // a column-major table in the workspace (64 rows per column, zero padded);
 // layout_rank reads the whole table as 1 KiB per wave instruction, 16 lanes
 // (one DPP row) per column, and row-reduces each column into its total and
 // its part before this block.  The kernel boundary is the only
 // synchronisation between blocks.
 //
-// Ranking, in both paths: the block's entries are split into one contiguous
+// Ranking a block: its entries are split into one contiguous
 // run per ranking wave.  A wave loads its run's ids into registers before
 // anything else, so its own histogram (per-wave counts in LDS) is built while
 // the table loads are still in flight.  After one barrier, wave 0 scans the
@@ -37,85 +36,58 @@
 // independent of workgroup scheduling.
 
 #include "ep_layout_dev.h"
+#include "ep_small_dev.h"
 
 namespace ep {
 namespace {
 
 using namespace layout;
 
-// ---- single-pass path --------------------------------------------------------
+// ---- small tables: one kernel --------------------------------------------------
 
-__global__ __launch_bounds__(kRankThreads) void layout_single_kernel(
-        const int32_t* __restrict__ idx, int64_t n, int E, int cap, int chunk, int nblocks,
-        int64_t R, int32_t* __restrict__ count, int32_t* __restrict__ offset,
-        int32_t* __restrict__ slot_of, int32_t* __restrict__ src_of_slot,
-        int32_t* __restrict__ status) {
-    extern __shared__ __align__(16) int32_t sm[];
-    __shared__ int32_t s_invalid, s_dropped;
-    const RankLds l = carve(sm, E);
+// Workgroup b ranks entries [64b, 64b + 64); the whole table is staged in its
+// LDS (ep_small_dev.h).
+__global__ __launch_bounds__(small::kThreads) void layout_small_kernel(
+        const int32_t* __restrict__ idx, int n, int E, int cap, int64_t R, int nwg,
+        int32_t* __restrict__ count, int32_t* __restrict__ offset, int32_t* __restrict__ slot_of,
+        int32_t* __restrict__ src_of_slot, int32_t* __restrict__ status) {
+    __shared__ int32_t s_eq[small::kMaxEntries];
+    __shared__ int32_t s_drop;
+    extern __shared__ __align__(16) int32_t s_dyn[];
+    const small::Tables tab = small::carve(s_dyn, n, E);
+    const int b = blockIdx.x;
     const int tid = threadIdx.x;
-    const int wave = tid / kWave;
-    const uint32_t lane = lane_id();
-    const int rw = rank_waves(E);
-    const int64_t begin = static_cast<int64_t>(blockIdx.x) * chunk;
-    const int64_t end = (begin + chunk < n) ? begin + chunk : n;
-    const Run r = wave_run(begin, end, chunk, rw, wave);
-    int32_t key[kKeySteps];
-    load_pass(idx, r.wbegin, r.wend, lane, key);
+    const int a = b * small::kMaxEntries;  // this workgroup's first entry
+    const int cnt = max(0, min(small::kMaxEntries, n - a));
 
-    for (int e = tid; e < E; e += kRankThreads) {
-        l.total[e] = 0;
-        l.prior[e] = 0;
-    }
-    int32_t* wrun = l.run + wave * (E + 1);
-    if (wave < rw)
-        for (int e = lane; e <= E; e += kWave) wrun[e] = 0;
-    if (tid == 0) s_invalid = 0;
+    small::IdStage stage;
+    stage.load(idx, n);
+    stage.store(n, tab.ids);
+    small::zero_tables(tab, E);
+    if (tid < small::kMaxEntries) s_eq[tid] = 0;
     __syncthreads();
 
-    // Whole-table histogram, and the histogram of the entries before this
-    // block.  Each lane reads 16-byte groups of 4 entries, kGroups groups in
-    // flight per pass (idx is 16-byte aligned; the last, partial group is read
-    // entry by entry).
-    constexpr int kGroups = 8;
-    const int64_t ngroups = (n + 3) / 4;
-    const int4* idx4 = reinterpret_cast<const int4*>(idx);
-    int32_t invalid = 0;
-    for (int64_t g0 = 0; g0 < ngroups; g0 += kGroups * kRankThreads) {
-        int4 q[kGroups];
-#pragma unroll
-        for (int u = 0; u < kGroups; ++u) {
-            const int64_t g = g0 + u * kRankThreads + tid;
-            if (4 * g + 3 < n) {
-                q[u] = idx4[g];
-            } else {
-                q[u].x = (4 * g + 0 < n) ? idx[4 * g + 0] : E;
-                q[u].y = (4 * g + 1 < n) ? idx[4 * g + 1] : E;
-                q[u].z = (4 * g + 2 < n) ? idx[4 * g + 2] : E;
-                q[u].w = E;
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kGroups; ++u) {
-            const int64_t i0 = 4 * (g0 + u * kRankThreads + tid);
-            const int32_t k4[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                if (valid_id(k4[c], E)) {
-                    atomicAdd(&l.total[k4[c]], 1);
-                    if (i0 + c < begin) atomicAdd(&l.prior[k4[c]], 1);
-                } else if (i0 + c < n) {
-                    ++invalid;
-                }
-            }
-        }
-    }
-    if (invalid) atomicAdd(&s_invalid, invalid);
-    if (wave < rw) count_run(idx, r, key, lane, E, key_bits(E), wrun);
+    if (tid < cnt) small::mark_entry(tab, E, tid, tab.ids[a + tid]);
+    small::histogram(tab, n, E);
     __syncthreads();
 
-    finish_layout(blockIdx.x, idx, n, E, cap, nblocks, R, l, r, key, s_invalid, &s_dropped, count,
-                  offset, slot_of, src_of_slot, status);
+    // Entry q sits at position a + q: an id at position i is ahead of the
+    // entries q > i - a.
+    const uint64_t all = (cnt == 64) ? ~0ull : ((1ull << cnt) - 1);
+    auto ahead = [&](int i) -> uint64_t {
+        return (i < a) ? all : (all & (~0ull << (i - a + 1)));
+    };
+    small::count_ahead(tab, cnt > 0 ? a + cnt - 1 : 0, E, ahead, s_eq);
+    small::scan_offsets(tab, E, cap, &s_drop);
+    __syncthreads();
+
+    if (tid < cnt) {
+        const int32_t slot = small::slot_for(tab, E, cap, tab.ids[a + tid], s_eq[tid]);
+        slot_of[a + tid] = slot;
+        if (slot >= 0 && slot < R) src_of_slot[slot] = a + tid;
+    }
+    if (b == 0) small::write_totals(tab, E, s_drop, count, offset, status);
+    small::fill_empty_rows(tab, E, cap, R, b, nwg, src_of_slot);
 }
 
 // ---- two-pass path -----------------------------------------------------------
@@ -142,7 +114,7 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
 LayoutGeometry layout_geometry(const ep_problem& p) {
     LayoutGeometry g;
     g.entries = static_cast<int64_t>(p.num_tokens) * p.num_topk;
-    g.single_pass = g.entries <= kSinglePassMaxEntries;
+    g.single_pass = g.entries <= kFusedMaxEntries;
     // Up to 64 workgroups (single pass: each pays for the whole-table
     // histogram; two passes: the table has 64 rows per column).  Chunks are
     // multiples of 256 entries (16-byte groups of the histogram kernel, whole
@@ -175,10 +147,11 @@ hipError_t launch_layout(const ep_problem& p, const int32_t* topk_idx, const ep_
     const int E = p.num_experts;
     const int64_t R = (p.capacity == 0) ? g.entries : static_cast<int64_t>(E) * p.capacity;
     if (g.single_pass) {
-        hipLaunchKernelGGL(layout_single_kernel, dim3(g.blocks), dim3(kRankThreads),
-                           rank_lds_bytes(E), stream, topk_idx, g.entries, E, p.capacity,
-                           g.chunk, g.blocks, R, out.count, out.offset, out.slot_of,
-                           out.src_of_slot, out.status);
+        const int n = static_cast<int>(g.entries);
+        const int nwg = n > 0 ? (n + small::kMaxEntries - 1) / small::kMaxEntries : 1;
+        hipLaunchKernelGGL(layout_small_kernel, dim3(nwg), dim3(small::kThreads),
+                           small::lds_bytes(n, E), stream, topk_idx, n, E, p.capacity, R, nwg,
+                           out.count, out.offset, out.slot_of, out.src_of_slot, out.status);
         return hipGetLastError();
     }
     const size_t lds_hist = static_cast<size_t>(E + 1) * 4;

@@ -13,7 +13,6 @@ namespace layout {
 constexpr int kHistThreads = 256;             // layout_hist workgroup
 constexpr int kRankThreads = 1024;            // layout_rank / layout_single workgroup
 constexpr int kRankRunWords = 4112;           // LDS words for the per-wave running ranks
-constexpr int64_t kSinglePassMaxEntries = 8192;
 constexpr int kTwoPassMaxBlocks = 64;
 constexpr int kTableStride = kTwoPassMaxBlocks;  // rows per table column
 constexpr int kKeySteps = 4;                  // 64-entry steps of a run held in registers
