@@ -9,25 +9,26 @@
 //
 // Launch shape: one workgroup per (token, column tile).  A lane owns VPL
 // 16-byte pieces of the row, spaced one workgroup-width apart so that every
-// load and store instruction of a wave covers 1 KiB of contiguous memory.
-// Tiles are two waves wide with VPL chosen so a tile covers a whole row of up
-// to 8192 channels; lanes past the end of the row redo the last piece
-// (last 16-lane group for FP8) and store the same bytes to the same place,
-// which keeps the loads free of branches.  All VPL loads are issued before
+// load and store instruction of a wave covers contiguous memory (see
+// dispatch_shape for the tile sizes); lanes past the end of the row redo the
+// last piece (last 16-lane group for FP8) and store the same bytes to the
+// same place, which keeps the loads free of branches.  All VPL loads are issued before
 // any store, the row is read from HBM once however large k is, and the
 // token's k slots are uniform across the workgroup (scalar loads).  Receive
-// rows are written with non-temporal stores: they are not read again by this
-// kernel and should not evict other data from the caches.
+// rows and scales are written with non-temporal stores: they are not read
+// again by this kernel, and plain stores would leave them dirty in the caches
+// for the next kernels to write back.
 //
 // A slot of -1 (or one outside [0, R), which a layout of this problem never
 // holds) writes nothing.
 //
 // FP8: a lane holds 8 channels, so a 128-channel block is 16 adjacent lanes
 // (one DPP row).  The block maximum of |x| is reduced across the row, the
-// scale is amax / 448 (IEEE fp32 division), each channel is divided by it
-// (IEEE fp32 division) and encoded with round-to-nearest-even.  The block
-// scales of the tile are collected in LDS and written as one contiguous run
-// per slot.
+// scale is amax / 448 (IEEE fp32 division), and each channel gets the
+// round-to-nearest-even E4M3 code of its IEEE quotient by the scale, reached
+// with one reciprocal per 8 channels and a division only next to E4M3
+// rounding midpoints (quant8 in ep_dispatch_dev.h).  The block scales of the
+// tile are collected in LDS and written as one contiguous run per slot.
 
 #include "ep_dispatch_dev.h"
 #include "ep_internal.h"
@@ -84,20 +85,24 @@ TileShape row_tile_shape(int nvec, int vpl) {
 
 namespace {
 
-// For batches of 1024 tokens or more, dispatch tiles are two waves wide with
-// up to eight 16-byte pieces per lane, so one workgroup covers a whole row of
-// up to 1024 pieces (H = 8192 bf16); the pieces of a lane are all loaded before
-// the first store.
+// For batches of 1024 tokens or more, bf16 dispatch tiles are two waves wide
+// with up to eight 16-byte pieces per lane, so one workgroup covers a whole
+// row of up to 1024 pieces (H = 8192); FP8 tiles have two pieces per lane and
+// as many lanes as the row needs (up to 1024).  The pieces of a lane are all
+// loaded before the first store.
 struct DispatchShape {
     int vpl;
     TileShape tile;
 };
 
-DispatchShape dispatch_shape(int nvec, int T) {
+DispatchShape dispatch_shape(int nvec, int T, bool fp8) {
     // Few tokens (decode batches): wide workgroups, one piece per lane, so
     // that enough waves exist to keep HBM busy.
     if (T < 1024) return {1, row_tile_shape(nvec, 1)};
     if (nvec <= 128) return {1, {((nvec + 63) / 64) * 64, 1}};
+    // FP8: quantising holds each piece's raw and encoded forms at once, so two
+    // pieces per lane keep the kernel at full occupancy (eight waves per SIMD).
+    if (fp8) return {2, row_tile_shape(nvec, 2)};
     const int vpl = two_wave_vpl(nvec);
     return {vpl, {128, (nvec + 128 * vpl - 1) / (128 * vpl)}};
 }
@@ -127,7 +132,7 @@ hipError_t launch_dispatch(const ep_problem& p, const void* x, const int32_t* sl
     const int nvec = p.hidden / 8;
     const int64_t R = p.capacity == 0 ? static_cast<int64_t>(T) * p.num_topk
                                       : static_cast<int64_t>(p.num_experts) * p.capacity;
-    const DispatchShape ds = dispatch_shape(nvec, T);
+    const DispatchShape ds = dispatch_shape(nvec, T, p.use_fp8 != 0);
     const dim3 grid(T, ds.tile.tiles);
     const int th = ds.tile.threads;
     switch (ds.vpl) {

@@ -11,8 +11,9 @@
 //
 // FP8: a lane holds 8 channels, so a 128-channel block is 16 adjacent lanes
 // (one DPP row).  The block maximum of |x| is reduced across the row, the
-// scale is amax / 448 (IEEE fp32 division), each channel is divided by it
-// (IEEE fp32 division) and encoded with round-to-nearest-even.
+// scale is amax / 448 (IEEE fp32 division), and each channel gets the
+// round-to-nearest-even E4M3 code of its IEEE fp32 quotient by the scale
+// (see quant8 for how that is reached with one division per 8 channels).
 #pragma once
 
 #include "ep_device.h"
@@ -62,15 +63,49 @@ __device__ __forceinline__ float row16_max(float m) {
     return m;
 }
 
-__device__ __forceinline__ uint32_t quant4(uint32_t w0, uint32_t w1, float scale) {
-    const float f[4] = {bf16_lo(w0), bf16_hi(w0), bf16_lo(w1), bf16_hi(w1)};
-    uint32_t packed = 0;
+// E4M3 codes of the 8 channels of one 16-byte piece, each the code of the
+// IEEE quotient fl(f / scale) (scale == 0: all codes 0).
+//
+// Dividing every channel is the ALU cost of FP8 dispatch, so the quotients
+// come from one IEEE reciprocal per piece instead: r = fl(1 / scale) and
+// p = fl(f * r) carry two roundings of relative error <= 2^-24 each, so p is
+// within 3 ulps of fl(f / scale).  The code of a quotient of E4M3-normal size
+// (>= 2^-6) changes only where the quotient crosses a midpoint between two
+// E4M3 values, which in fp32 bits is low 20 bits == 0x80000; a zero quotient
+// is exact.  A channel whose p is a zero, or at least 2^-6 and more than 8
+// ulps from a midpoint, therefore has the code of p.  The others (near a
+// midpoint, below 2^-6, or r not finite because scale is tiny) are divided,
+// in a branch that a wave takes only when one of its lanes needs it.
+__device__ __forceinline__ u32x2 quant8(const u32x4& w, float scale) {
+    const float f[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                        bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+    uint32_t code[8];
+    uint32_t exact = 0;  // channels that need the division
+    if (scale == 0.0f) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t c = (scale == 0.0f) ? 0u : f32_to_e4m3_rne(f[i] / scale);
-        packed |= c << (8 * i);
+        for (int i = 0; i < 8; ++i) code[i] = 0;
+    } else {
+        const float r = 1.0f / scale;
+        const bool r_ok = __float_as_uint(r) < 0x7f800000u;  // finite (r > 0)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p = f[i] * r;
+            const uint32_t a = __float_as_uint(p) & 0x7fffffffu;
+            const int mid = static_cast<int>(a & 0xfffffu) - 0x80000;
+            const bool ok = r_ok && (a == 0 || (a >= 0x3c800000u && (mid > 8 || mid < -8)));
+            code[i] = f32_to_e4m3_rne(p);
+            exact |= ok ? 0u : (1u << i);
+        }
+        if (__ballot(exact != 0)) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (exact & (1u << i)) code[i] = f32_to_e4m3_rne(f[i] / scale);
+        }
     }
-    return packed;
+    u32x2 q;
+    q.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+    q.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+    return q;
 }
 
 __device__ __forceinline__ float absmax8(const u32x4& p) {
@@ -114,8 +149,7 @@ struct Fp8Tile {
         for (int u = 0; u < VPL; ++u) {
             const float amax = row16_max(absmax8(buf[u]));
             const float scale = amax / 448.0f;
-            q[u].x = quant4(buf[u].x, buf[u].y, scale);
-            q[u].y = quant4(buf[u].z, buf[u].w, scale);
+            q[u] = quant8(buf[u], scale);
             const int vv = tile0 + u * gsize + gtid;
             if ((gtid & 15) == 0 && vv < nvec) s_scale[(vv - tile0) >> 4] = scale;
         }
@@ -151,7 +185,7 @@ __device__ __forceinline__ void fp8_store_scales(const float* s_scale, const int
         const int b = i - j * nb;
         const int32_t slot = slots[j];
         if (slot >= 0 && slot < R)
-            recv_scales[static_cast<int64_t>(slot) * nblk + b0 + b] = s_scale[b];
+            __builtin_nontemporal_store(s_scale[b], recv_scales + static_cast<int64_t>(slot) * nblk + b0 + b);
     }
 }
 

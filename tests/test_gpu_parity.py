@@ -265,6 +265,53 @@ def test_fp8_special_rows():
         check_case(c, run_gpu(c, fused=True))
 
 
+def _near_midpoint_rows(T, H, seed, tries=150):
+    """bf16 rows whose 128-channel blocks have a non-power-of-two scale and
+    many channels whose quotient by it lies within 8 fp32 ulps of a midpoint
+    between two E4M3 values: the channels the dispatch kernel must divide
+    instead of multiplying by the reciprocal.  (With bf16 inputs a quotient
+    is either that close to a midpoint, through the rounding of the scale, or
+    about 2^11 ulps or more away, so these are the cases that matter.)  For
+    each block the block maximum is picked, among `tries` random bf16
+    values, as the one giving the most such quotients."""
+    rng = np.random.default_rng(seed)
+    pos = (np.arange(0x0080, 0x7F80, dtype=np.uint32) << 16).view(np.float32)  # normal bf16 > 0
+    pos = pos[pos < 512.0]
+    xf = np.empty((T, H), np.float32)
+    for t in range(T):
+        for b in range(H // 128):
+            best = None
+            for amax in rng.choice(pos[pos > 0.25], tries):
+                amax = np.float32(amax)
+                scale = np.float32(amax / np.float32(448.0))
+                if scale.view(np.uint32) & 0x7FFFFF == 0:
+                    continue  # power-of-two scale: exact quotients
+                cand = pos[pos < amax]
+                q = (cand / scale).astype(np.float32)
+                d = np.abs((q.view(np.uint32) & 0xFFFFF).astype(np.int64) - 0x80000)
+                near = cand[(d <= 8) & (q >= 2.0 ** -6)]
+                if best is None or near.size > best[1].size:
+                    best = (amax, near, cand)
+            amax, near, cand = best
+            blk = np.concatenate([near, rng.choice(cand, 128)])[:128]
+            blk = blk * rng.choice(np.float32([-1, 1]), 128)
+            blk[int(rng.integers(128))] = amax
+            xf[t, 128 * b:128 * (b + 1)] = blk
+    return workloads.to_bf16_bits(xf)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+def test_fp8_near_midpoint_quotients(fused):
+    T, H, E, k = 8, 1024, 8, 2
+    x = _near_midpoint_rows(T, H, seed=77)
+    rng = np.random.default_rng(78)
+    ids = np.stack([np.arange(T) % E, (np.arange(T) + 3) % E], axis=1).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    eo = workloads.to_bf16_bits(rng.standard_normal((T * k, H)).astype(np.float32))
+    c = Case(T, H, k, E, 0, True, x, ids, w, eo, name="fp8_near_midpoint")
+    check_case(c, run_gpu(c, fused=fused))
+
+
 @pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
 def test_non_default_stream(fused):
     c = _random_case(333, 512, 4, 16, 0, True, seed=5, name="side_stream")
