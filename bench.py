@@ -52,10 +52,21 @@ def algorithmic_bytes(wl, count=None):
 
 
 def kernel_source_digest(name):
-    path = os.path.join(ROOT, "combine_ep_layout_09_amd", "csrc", name)
+    """Digest of a kernel source file and every csrc header it includes,
+    directly or not (quoted includes)."""
+    csrc = os.path.join(ROOT, "combine_ep_layout_09_amd", "csrc")
+    seen, todo = [], [name]
+    while todo:
+        f = todo.pop(0)
+        if f in seen or not os.path.exists(os.path.join(csrc, f)):
+            continue
+        seen.append(f)
+        for line in open(os.path.join(csrc, f)):
+            if line.startswith('#include "'):
+                todo.append(line.split('"')[1])
     h = hashlib.sha256()
-    for f in (path, os.path.join(ROOT, "combine_ep_layout_09_amd", "csrc", "ep_device.h")):
-        with open(f, "rb") as fh:
+    for f in sorted(seen):
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
