@@ -125,6 +125,8 @@ def layout(topk_idx, E, cap=0):
 def dispatch(x_bf16, slot_of, R, use_fp8, recv_x=None, recv_scales=None, t0=0, t1=None):
     """Scatter (and optionally quantise) token rows into receive rows.
 
+    use_fp8: 0 bf16 rows; 1 E4M3FN rows + fp32 scales [R, H/128]; 2 E4M3FN rows
+    + UE8M0 scale bytes [R, H/128].
     x_bf16 uint16 [T, H]; slot_of int32 [T, k].  recv_x / recv_scales may be
     passed pre-filled (rows no entry maps to keep their contents); otherwise
     they are created filled with 0xFF bytes.  Returns (recv_x, recv_scales).
@@ -134,16 +136,20 @@ def dispatch(x_bf16, slot_of, R, use_fp8, recv_x=None, recv_scales=None, t0=0, t
     T, H = x.shape
     k = s.shape[1]
     t1 = T if t1 is None else t1
-    if use_fp8:
+    mode = int(use_fp8)
+    if mode not in (0, 1, 2):
+        raise ValueError("use_fp8 must be 0 (bf16), 1 (fp32 scales) or 2 (UE8M0 scales)")
+    if mode:
         if recv_x is None:
             recv_x = np.full((R, H), 0xFF, np.uint8)
         if recv_scales is None:
-            recv_scales = np.full((R, H // 128), -1, np.int32).view(np.float32)
+            recv_scales = (np.full((R, H // 128), -1, np.int32).view(np.float32) if mode == 1
+                           else np.full((R, H // 128), 0xFF, np.uint8))
     else:
         if recv_x is None:
             recv_x = np.full((R, H), 0xFFFF, np.uint16)
-    rc = _load().orc_dispatch(T, H, k, R, int(bool(use_fp8)), t0, t1, _ptr(x), _ptr(s),
-                              _ptr(recv_x), _ptr(recv_scales) if use_fp8 else None)
+    rc = _load().orc_dispatch(T, H, k, R, mode, t0, t1, _ptr(x), _ptr(s),
+                              _ptr(recv_x), _ptr(recv_scales) if mode else None)
     if rc != 0:
         raise ValueError("orc_dispatch rejected its arguments")
     return recv_x, (recv_scales if use_fp8 else None)

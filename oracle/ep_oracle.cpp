@@ -26,7 +26,9 @@
 // * The arithmetic itself (one fp32 scale per 128 channels, scale = amax/448,
 //   OCP E4M3FN round-to-nearest-even, fp32 weighted sum rounded to bf16 with a
 //   fixed top-k order) is not on the pages; it is the definition this library
-//   implements and is written out below exactly as defined.
+//   implements and is written out below exactly as defined.  The UE8M0 scale
+//   variant is named on the pages ("[PR #206] [MERGED] Support UE8M0 data
+//   format") and read as a power-of-two scale held as its exponent byte.
 //
 // Parity pins (what checks this file against something other than itself)
 // live in tests/test_oracle_pins.py.
@@ -222,16 +224,25 @@ int orc_layout(int32_t T, int32_t k, int32_t E, int32_t cap, const int32_t* topk
 //       scale = amax / 448                           (one IEEE fp32 division)
 //       q[c]  = E4M3FN_RNE_saturating(x[c] / scale)  (fp32 division, then encode)
 //     amax == 0 gives scale = 0 and every code 0x00 (the quotient is 0/0).
+//   use_fp8 = 2: as 1, but each block's scale is a power of two held as one
+//     UE8M0 byte (an unsigned 8-bit exponent, value 2^(byte - 127)); the format
+//     is named, not defined, in "[PR #206] [MERGED] Support UE8M0 data format".
+//     Reading: the scale is the smallest power of two 2^s, s >= -127, with
+//     448 * 2^s >= amax, so no quotient exceeds 448 (as with the fp32 scale);
+//     recv_scales holds the bytes s + 127, [R, H/128].  The quotient x / 2^s is
+//     exact.  amax == 0 gives byte 0 and every code 0x00.
 // x is bf16 [T, H].  Receive rows that no entry maps to are not touched.
 // Returns 0, or -1 for bad sizes.
 int orc_dispatch(int32_t T, int32_t H, int32_t k, int64_t R, int32_t use_fp8, int32_t t0,
                  int32_t t1, const uint16_t* x, const int32_t* slot_of, void* recv_x,
-                 float* recv_scales) {
+                 void* recv_scales) {
     if (T < 0 || H < 1 || k < 1 || t0 < 0 || t1 > T || t0 > t1) return -1;
+    if (use_fp8 < 0 || use_fp8 > 2) return -1;
     if (use_fp8 && H % 128 != 0) return -1;
     const int32_t nblk = H / 128;
     std::vector<uint8_t> q(static_cast<size_t>(H));
     std::vector<float> scales(static_cast<size_t>(use_fp8 ? nblk : 0));
+    std::vector<uint8_t> exps(static_cast<size_t>(use_fp8 ? nblk : 0));
     for (int32_t t = t0; t < t1; ++t) {
         const uint16_t* xt = x + static_cast<int64_t>(t) * H;
         if (use_fp8) {
@@ -243,7 +254,18 @@ int orc_dispatch(int32_t T, int32_t H, int32_t k, int64_t R, int32_t use_fp8, in
                     float av = std::fabs(v);
                     if (av > amax) amax = av;
                 }
-                float scale = amax / 448.0f;
+                float scale;
+                if (use_fp8 == 1) {
+                    scale = amax / 448.0f;
+                } else if (amax == 0.0f) {
+                    scale = 0.0f;
+                    exps[b] = 0;
+                } else {
+                    int s = -127;  // step up to the first power of two that is large enough
+                    while (448.0 * std::ldexp(1.0, s) < static_cast<double>(amax)) ++s;
+                    scale = std::ldexp(1.0f, s);
+                    exps[b] = static_cast<uint8_t>(s + 127);
+                }
                 scales[b] = scale;
                 for (int32_t c = 0; c < 128; ++c) {
                     float v = bf16_bits_to_float(xt[b * 128 + c]);
@@ -258,8 +280,12 @@ int orc_dispatch(int32_t T, int32_t H, int32_t k, int64_t R, int32_t use_fp8, in
             if (use_fp8) {
                 uint8_t* dst = static_cast<uint8_t*>(recv_x) + static_cast<int64_t>(slot) * H;
                 std::memcpy(dst, q.data(), static_cast<size_t>(H));
-                std::memcpy(recv_scales + static_cast<int64_t>(slot) * nblk, scales.data(),
-                            sizeof(float) * static_cast<size_t>(nblk));
+                if (use_fp8 == 1)
+                    std::memcpy(static_cast<float*>(recv_scales) + static_cast<int64_t>(slot) * nblk,
+                                scales.data(), sizeof(float) * static_cast<size_t>(nblk));
+                else
+                    std::memcpy(static_cast<uint8_t*>(recv_scales) + static_cast<int64_t>(slot) * nblk,
+                                exps.data(), static_cast<size_t>(nblk));
             } else {
                 uint16_t* dst = static_cast<uint16_t*>(recv_x) + static_cast<int64_t>(slot) * H;
                 std::memcpy(dst, xt, sizeof(uint16_t) * static_cast<size_t>(H));

@@ -27,7 +27,11 @@ MUTANTS = {
     "e4m3_drop_negative_zero": ("uint8_t sign = std::signbit(f) ? 0x80 : 0x00;",
                                 "uint8_t sign = (f < 0.0f) ? 0x80 : 0x00;"),
     "bf16_tie_to_odd": ("else pick = (lo % 2 == 0) ? lo : hi;", "else pick = (lo % 2 == 0) ? hi : lo;"),
-    "scale_constant": ("float scale = amax / 448.0f;", "float scale = amax / 440.0f;"),
+    "scale_constant": ("scale = amax / 448.0f;", "scale = amax / 440.0f;"),
+    "ue8m0_strict_bound": ("while (448.0 * std::ldexp(1.0, s) < static_cast<double>(amax)) ++s;",
+                           "while (448.0 * std::ldexp(1.0, s) <= static_cast<double>(amax)) ++s;"),
+    "ue8m0_bias": ("exps[b] = static_cast<uint8_t>(s + 127);", "exps[b] = static_cast<uint8_t>(s + 128);"),
+    "ue8m0_no_clamp_at_2_pow_minus_127": ("int s = -127;", "int s = -126;"),
     "scale_reciprocal_multiply": ("e4m3_encode(v / scale)", "e4m3_encode(v * (1.0f / scale))"),
     "scale_block_shift": ("float v = bf16_bits_to_float(xt[b * 128 + c]);\n                    assert",
                           "float v = bf16_bits_to_float(xt[(b * 128 + c + 1) % H]);\n                    assert"),
@@ -58,6 +62,7 @@ def _fast_pins():
         pins.test_bf16_named,
         pins.test_dispatch_fp8_exact_when_scale_is_power_of_two,
         pins.test_dispatch_fp8_near_ties_vs_exact_rational,
+        pins.test_dispatch_ue8m0_vs_exact_exponent_and_torch,
         pins.test_combine_single_term_is_gather,
         pins.test_combine_fma_chain_vs_exact_rational,
         pins.test_combine_skips_unplaced_entries,

@@ -329,6 +329,72 @@ def test_dispatch_fp8_exact_when_scale_is_power_of_two():
             np.testing.assert_array_equal(q[r][zero], np.where(np.signbit(xf[t][zero]), 0x80, 0x00))
 
 
+def _ue8m0_blocks(rng, T, H):
+    """bf16 rows whose blocks have maxima at exactly 448*2^j, one bf16 step
+    either side of it, random normals, bf16 subnormals (below 448*2^-127,
+    where the exponent is clamped), and all-zero blocks."""
+    nblk = H // 128
+    xf = (rng.standard_normal((T, H)) * 2.0 ** rng.integers(-30, 30, size=(T, 1))).astype(np.float32)
+    for t in range(T):
+        for b in range(nblk):
+            sl = slice(128 * b, 128 * b + 128)
+            kind = (t * nblk + b) % 6
+            j = int(rng.integers(-100, 100))
+            if kind == 0:
+                amax = np.float32(448.0 * 2.0 ** j)
+            elif kind in (1, 2):
+                base = np.float32(448.0 * 2.0 ** j).view(np.uint32)
+                amax = (base + (1 << 16) if kind == 1 else base - (1 << 16)).view(np.float32)
+            elif kind == 3:
+                xf[t, sl] = ((rng.integers(1, 128, 128).astype(np.uint32) << 16).view(np.float32)
+                             * rng.choice(np.float32([-1, 1]), 128))
+                continue
+            elif kind == 4:
+                xf[t, sl] = 0.0
+                continue
+            else:
+                continue
+            xf[t, sl] = np.clip(xf[t, sl], -amax * 0.99, amax * 0.99)
+            xf[t, 128 * b + int(rng.integers(128))] = amax * rng.choice([-1, 1])
+    return workloads.to_bf16_bits(xf)
+
+
+def test_dispatch_ue8m0_vs_exact_exponent_and_torch():
+    """UE8M0 scales: the exponent byte is the smallest s >= -127 with
+    448 * 2^s >= amax, checked with exact rationals; every code is torch's
+    float8_e4m3fn conversion of x * 2^-s (a power-of-two scaling, exact in
+    float64); all-zero blocks give byte 0 and codes 0x00."""
+    from fractions import Fraction
+    rng = np.random.default_rng(31)
+    T, H = 24, 768
+    nblk = H // 128
+    x = _ue8m0_blocks(rng, T, H)
+    xf = oracle.bf16_to_float(x)
+    idx = np.stack([np.arange(T) % 4, 4 + np.arange(T) % 3], axis=1).astype(np.int32)
+    lay = oracle.layout(idx, 7, 0)
+    q, e = oracle.dispatch(x, lay["slot_of"], T * 2, 2)
+    assert e.dtype == np.uint8
+    for t in range(T):
+        want_e = np.empty(nblk, np.uint8)
+        want_q = np.empty(H, np.uint8)
+        for b in range(nblk):
+            blk = xf[t, 128 * b:128 * (b + 1)].astype(np.float64)
+            amax = Fraction(float(np.abs(blk).max()))
+            if amax == 0:
+                want_e[b], want_q[128 * b:128 * (b + 1)] = 0, 0
+                continue
+            s = -127
+            while Fraction(448) * Fraction(2) ** s < amax:
+                s += 1
+            want_e[b] = s + 127
+            scaled = torch.from_numpy(blk * 2.0 ** -s).to(torch.float32)
+            want_q[128 * b:128 * (b + 1)] = scaled.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        for j in range(2):
+            r = lay["slot_of"][t, j]
+            np.testing.assert_array_equal(e[r], want_e)
+            np.testing.assert_array_equal(q[r], want_q)
+
+
 def test_dispatch_fp8_near_ties_vs_exact_rational():
     """Blocks whose quotients x/scale fall next to E4M3 rounding midpoints --
     the inputs where the order of rounding matters most.  Expected values are
