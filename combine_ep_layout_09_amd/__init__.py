@@ -49,7 +49,8 @@ class EpError(RuntimeError):
 
 
 class Problem(ctypes.Structure):
-    """ep_problem: T, H, k, E, capacity (0 = contiguous), use_fp8."""
+    """ep_problem: T, H, k, E, capacity (0 = contiguous), use_fp8 (0 bf16,
+    1 E4M3FN + fp32 scales, 2 E4M3FN + UE8M0 scale bytes)."""
     _fields_ = [("num_tokens", ctypes.c_int32), ("hidden", ctypes.c_int32),
                 ("num_topk", ctypes.c_int32), ("num_experts", ctypes.c_int32),
                 ("capacity", ctypes.c_int32), ("use_fp8", ctypes.c_int32)]
@@ -195,13 +196,18 @@ def alloc_workspace(prob, device="cuda"):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def _scale_dtype(prob):
+    """Block-scale element type: fp32 (use_fp8 = 1) or UE8M0 bytes (use_fp8 = 2)."""
+    return _torch().uint8 if prob.use_fp8 == 2 else _torch().float32
+
+
 def alloc_recv(prob, device="cuda"):
     """Receive buffers for dispatch: (recv_x, recv_scales or None)."""
     torch = _torch()
     R = ep_num_recv_rows(prob)
     if prob.use_fp8:
         return (torch.empty((R, prob.hidden), dtype=torch.uint8, device=device),
-                torch.empty((R, prob.hidden // 128), dtype=torch.float32, device=device))
+                torch.empty((R, prob.hidden // 128), dtype=_scale_dtype(prob), device=device))
     return torch.empty((R, prob.hidden), dtype=torch.bfloat16, device=device), None
 
 
@@ -231,7 +237,7 @@ def ep_dispatch(prob, x, layout, recv_x, recv_scales=None, stream=None):
     xp = _ptr(x, "x", torch.bfloat16, T * H, allow_none=True)
     if prob.use_fp8:
         rp = _ptr(recv_x, "recv_x", (torch.uint8, torch.float8_e4m3fn), R * H, allow_none=True)
-        sp = _ptr(recv_scales, "recv_scales", torch.float32, R * (H // 128), allow_none=True)
+        sp = _ptr(recv_scales, "recv_scales", _scale_dtype(prob), R * (H // 128), allow_none=True)
     else:
         rp = _ptr(recv_x, "recv_x", torch.bfloat16, R * H, allow_none=True)
         sp = None
@@ -250,7 +256,7 @@ def _layout_dispatch_args(prob, topk_idx, layout, workspace, x, recv_x, recv_sca
     nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if prob.use_fp8:
         rp = _ptr(recv_x, "recv_x", (torch.uint8, torch.float8_e4m3fn), R * H, allow_none=True)
-        sp = _ptr(recv_scales, "recv_scales", torch.float32, R * (H // 128), allow_none=True)
+        sp = _ptr(recv_scales, "recv_scales", _scale_dtype(prob), R * (H // 128), allow_none=True)
     else:
         rp = _ptr(recv_x, "recv_x", torch.bfloat16, R * H, allow_none=True)
         sp = None
@@ -317,7 +323,7 @@ def prepare_dispatch(prob, x, layout, recv_x, recv_scales=None):
     s = layout._struct(prob, check_all=False)
     if prob.use_fp8:
         rp = _ptr(recv_x, "recv_x", (torch.uint8, torch.float8_e4m3fn), R * H, allow_none=True)
-        sp = _ptr(recv_scales, "recv_scales", torch.float32, R * (H // 128), allow_none=True)
+        sp = _ptr(recv_scales, "recv_scales", _scale_dtype(prob), R * (H // 128), allow_none=True)
     else:
         rp = _ptr(recv_x, "recv_x", torch.bfloat16, R * H, allow_none=True)
         sp = None

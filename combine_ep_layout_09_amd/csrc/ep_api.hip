@@ -17,7 +17,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 int check_problem(const ep_problem* p) {
     if (p == nullptr) return EP_ERR_ARG;
     if (p->num_tokens < 0 || p->hidden < 1 || p->num_topk < 1 || p->num_experts < 1 ||
-        p->capacity < 0 || (p->use_fp8 != 0 && p->use_fp8 != 1))
+        p->capacity < 0 || p->use_fp8 < 0 || p->use_fp8 > 2)
         return EP_ERR_ARG;
     if (p->num_experts > ep::kMaxExperts || p->num_topk > ep::kMaxTopk ||
         p->hidden > ep::kMaxHidden || p->hidden % 8 != 0 ||
@@ -84,7 +84,7 @@ int ep_layout(const ep_problem* prob, const int32_t* topk_idx, const ep_layout_t
 }
 
 int ep_dispatch(const ep_problem* prob, const void* x, const ep_layout_t* layout, void* recv_x,
-                float* recv_scales, void* stream) {
+                void* recv_scales, void* stream) {
     int rc = check_problem(prob);
     if (rc != EP_OK) return rc;
     rc = check_layout_ptrs(*prob, layout, false);
@@ -102,7 +102,7 @@ int ep_dispatch(const ep_problem* prob, const void* x, const ep_layout_t* layout
 
 int ep_layout_dispatch(const ep_problem* prob, const int32_t* topk_idx, const ep_layout_t* out,
                        void* workspace, size_t workspace_bytes, const void* x, void* recv_x,
-                       float* recv_scales, void* stream) {
+                       void* recv_scales, void* stream) {
     int rc = check_problem(prob);
     if (rc != EP_OK) return rc;
     rc = check_layout_ptrs(*prob, out, true);

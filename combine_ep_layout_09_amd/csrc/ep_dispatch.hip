@@ -49,19 +49,23 @@ __global__ __launch_bounds__(kMaxThreads) void dispatch_bf16_kernel(
     tile.store(slot_of + static_cast<int64_t>(blockIdx.x) * k, k, R, recv, nvec);
 }
 
-template <int VPL>
+template <int VPL, bool UE8M0>
 __global__ __launch_bounds__(kMaxThreads) void dispatch_fp8_kernel(
         const u32x4* __restrict__ x, int nvec, int nblk, int k,
         const int32_t* __restrict__ slot_of, int64_t R, u32x2* __restrict__ recv_q,
-        float* __restrict__ recv_scales) {
+        void* __restrict__ recv_scales) {
     extern __shared__ float s_scale[];  // [blockDim * VPL / 16] scales of this tile
     const int32_t* slots = slot_of + static_cast<int64_t>(blockIdx.x) * k;
-    Fp8Tile<VPL> tile;
+    Fp8Tile<VPL, UE8M0> tile;
     tile.load_quantise(x, nvec, blockIdx.x, blockIdx.y, blockDim.x, threadIdx.x, s_scale);
     tile.store(slots, k, R, recv_q, nvec);
     __syncthreads();
-    fp8_store_scales(s_scale, slots, k, R, recv_scales, nblk, blockIdx.y, blockDim.x, VPL,
-                     threadIdx.x);
+    if (UE8M0)
+        fp8_store_scales(s_scale, slots, k, R, static_cast<uint8_t*>(recv_scales), nblk,
+                         blockIdx.y, blockDim.x, VPL, threadIdx.x);
+    else
+        fp8_store_scales(s_scale, slots, k, R, static_cast<float*>(recv_scales), nblk,
+                         blockIdx.y, blockDim.x, VPL, threadIdx.x);
 }
 
 // Elementwise use of the same encoder, for callers that quantise other data.
@@ -109,13 +113,18 @@ DispatchShape dispatch_shape(int nvec, int T, bool fp8) {
 
 template <int VPL>
 void launch_vpl(const ep_problem& p, dim3 grid, int threads, const void* x, int nvec,
-                const int32_t* slot_of, int64_t R, void* recv_x, float* recv_scales,
+                const int32_t* slot_of, int64_t R, void* recv_x, void* recv_scales,
                 hipStream_t stream) {
     if (p.use_fp8) {
         const size_t lds = static_cast<size_t>(threads) * VPL / 16 * 4;
-        hipLaunchKernelGGL(dispatch_fp8_kernel<VPL>, grid, dim3(threads), lds, stream,
-                           static_cast<const u32x4*>(x), nvec, p.hidden / 128, p.num_topk,
-                           slot_of, R, static_cast<u32x2*>(recv_x), recv_scales);
+        if (p.use_fp8 == 2)
+            hipLaunchKernelGGL((dispatch_fp8_kernel<VPL, true>), grid, dim3(threads), lds, stream,
+                               static_cast<const u32x4*>(x), nvec, p.hidden / 128, p.num_topk,
+                               slot_of, R, static_cast<u32x2*>(recv_x), recv_scales);
+        else
+            hipLaunchKernelGGL((dispatch_fp8_kernel<VPL, false>), grid, dim3(threads), lds, stream,
+                               static_cast<const u32x4*>(x), nvec, p.hidden / 128, p.num_topk,
+                               slot_of, R, static_cast<u32x2*>(recv_x), recv_scales);
     } else {
         hipLaunchKernelGGL(dispatch_bf16_kernel<VPL>, grid, dim3(threads), 0, stream,
                            static_cast<const u32x4*>(x), nvec, p.num_topk, slot_of, R,
@@ -126,7 +135,7 @@ void launch_vpl(const ep_problem& p, dim3 grid, int threads, const void* x, int 
 }  // namespace
 
 hipError_t launch_dispatch(const ep_problem& p, const void* x, const int32_t* slot_of,
-                           void* recv_x, float* recv_scales, hipStream_t stream) {
+                           void* recv_x, void* recv_scales, hipStream_t stream) {
     const int T = p.num_tokens;
     if (T == 0) return hipSuccess;
     const int nvec = p.hidden / 8;

@@ -108,6 +108,32 @@ __device__ __forceinline__ u32x2 quant8(const u32x4& w, float scale) {
     return q;
 }
 
+// UE8M0 block scale: the exponent s of the smallest power of two 2^s,
+// s >= -127, with 448 * 2^s >= amax (>= 0).  For amax = (1 + M/2^23) 2^e,
+// amax / 448 = ((1 + M/2^23) / 1.75) 2^(e-8), and the first factor lies in
+// (0.57, 1] when M <= 0x600000 (1.75 = 1 + 0x600000/2^23) and in (1, 1.15)
+// otherwise; subnormal and zero amax fall to the clamp.
+__device__ __forceinline__ int ue8m0_exponent(float amax) {
+    const uint32_t b = __float_as_uint(amax);
+    const int s = static_cast<int>(b >> 23) - 127 - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
+    return s < -127 ? -127 : s;
+}
+
+// E4M3 codes of the 8 channels of one piece scaled by a power of two
+// (factor = 2^-s: the product is exact, so this is the code of x / 2^s); an
+// all-zero block gives all codes 0.
+__device__ __forceinline__ u32x2 quant8_pow2(const u32x4& w, float factor, bool zero_block) {
+    const float f[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                        bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+    uint32_t code[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) code[i] = zero_block ? 0u : f32_to_e4m3_rne(f[i] * factor);
+    u32x2 q;
+    q.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
+    q.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+    return q;
+}
+
 __device__ __forceinline__ float absmax8(const u32x4& p) {
     float m = fabsf(bf16_lo(p.x));
     m = fmaxf(m, fabsf(bf16_hi(p.x)));
@@ -123,7 +149,9 @@ __device__ __forceinline__ float absmax8(const u32x4& p) {
 // nvec = H / 8 (a multiple of 16).  gsize is a multiple of 64, so 16-lane
 // groups never straddle the end of the row: a group past the end maps as a
 // whole onto the row's last group.
-template <int VPL>
+// UE8M0 = false: fp32 scale amax / 448 per block; true: power-of-two scale
+// held as its exponent byte (kept as a small float in s_scale).
+template <int VPL, bool UE8M0 = false>
 struct Fp8Tile {
     int v[VPL];
     u32x2 q[VPL];
@@ -148,10 +176,19 @@ struct Fp8Tile {
 #pragma unroll
         for (int u = 0; u < VPL; ++u) {
             const float amax = row16_max(absmax8(buf[u]));
-            const float scale = amax / 448.0f;
-            q[u] = quant8(buf[u], scale);
+            float stored;
+            if (UE8M0) {
+                const int s = ue8m0_exponent(amax);
+                const float factor = __uint_as_float(static_cast<uint32_t>(127 - s) << 23);
+                q[u] = quant8_pow2(buf[u], factor, amax == 0.0f);
+                stored = static_cast<float>(s + 127);
+            } else {
+                const float scale = amax / 448.0f;
+                q[u] = quant8(buf[u], scale);
+                stored = scale;
+            }
             const int vv = tile0 + u * gsize + gtid;
-            if ((gtid & 15) == 0 && vv < nvec) s_scale[(vv - tile0) >> 4] = scale;
+            if ((gtid & 15) == 0 && vv < nvec) s_scale[(vv - tile0) >> 4] = stored;
         }
     }
 
@@ -173,10 +210,12 @@ struct Fp8Tile {
     }
 };
 
-// Writes the tile's block scales (staged in s_scale by load_quantise, after a
-// barrier) as one contiguous run per slot.
+// Writes the tile's block scales (staged in s_scale by quantise, after a
+// barrier) as one contiguous run per slot: fp32 scales (S = float) or UE8M0
+// exponent bytes (S = uint8_t).
+template <typename S>
 __device__ __forceinline__ void fp8_store_scales(const float* s_scale, const int32_t* slots, int k,
-                                                 int64_t R, float* __restrict__ recv_scales,
+                                                 int64_t R, S* __restrict__ recv_scales,
                                                  int nblk, int tile, int gsize, int vpl, int gtid) {
     const int b0 = (tile * gsize * vpl) >> 4;
     const int nb = min(gsize * vpl / 16, nblk - b0);
@@ -185,7 +224,8 @@ __device__ __forceinline__ void fp8_store_scales(const float* s_scale, const int
         const int b = i - j * nb;
         const int32_t slot = slots[j];
         if (slot >= 0 && slot < R)
-            __builtin_nontemporal_store(s_scale[b], recv_scales + static_cast<int64_t>(slot) * nblk + b0 + b);
+            __builtin_nontemporal_store(static_cast<S>(s_scale[b]),
+                                        recv_scales + static_cast<int64_t>(slot) * nblk + b0 + b);
     }
 }
 

@@ -60,7 +60,7 @@ struct SmallParams {
     int32_t* status;
     const u32x4* x;
     void* recv_x;
-    float* recv_scales;
+    void* recv_scales;  // fp32 scales or UE8M0 bytes
     int T, k, nvec, tiles, nwg;
 };
 
@@ -73,8 +73,10 @@ __device__ inline uint64_t token_ahead(int i, int start, int k, int base) {
     return (d >= k) ? 0ull : (all & (~0ull << (base + d)));
 }
 
-template <int VPL, bool FP8>
+// MODE: 0 bf16 payload, 1 E4M3FN + fp32 scales, 2 E4M3FN + UE8M0 scales.
+template <int VPL, int MODE>
 __global__ __launch_bounds__(kThreads) void layout_dispatch_small_kernel(SmallParams p) {
+    constexpr bool FP8 = MODE != 0;
     __shared__ int32_t s_eq[small::kMaxEntries];
     __shared__ int32_t s_slot[kGroups][kMaxTopk];
     __shared__ int32_t s_drop;
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_small_kernel(SmallPa
     small::IdStage stage;
     stage.load(p.idx, p.n);
     Bf16Tile<VPL> bt;
-    Fp8Tile<VPL> ft;
+    Fp8Tile<VPL, MODE == 2> ft;
     if (active) {
         if (FP8) ft.load(p.x, p.nvec, t, tile, kGroupThreads, gtid);
         else bt.load(p.x, p.nvec, t, tile, kGroupThreads, gtid);
@@ -160,8 +162,14 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_small_kernel(SmallPa
         const int32_t* slots = s_slot[g];
         if (FP8) {
             ft.store(slots, k, p.R, static_cast<u32x2*>(p.recv_x), p.nvec);
-            dispatch::fp8_store_scales(s_scale[g], slots, k, p.R, p.recv_scales, p.nvec / 16, tile,
-                                       kGroupThreads, VPL, gtid);
+            if (MODE == 2)
+                dispatch::fp8_store_scales(s_scale[g], slots, k, p.R,
+                                           static_cast<uint8_t*>(p.recv_scales), p.nvec / 16,
+                                           tile, kGroupThreads, VPL, gtid);
+            else
+                dispatch::fp8_store_scales(s_scale[g], slots, k, p.R,
+                                           static_cast<float*>(p.recv_scales), p.nvec / 16, tile,
+                                           kGroupThreads, VPL, gtid);
         } else {
             bt.store(slots, k, p.R, static_cast<u32x4*>(p.recv_x), p.nvec);
         }
@@ -170,13 +178,16 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_small_kernel(SmallPa
 }
 
 template <int VPL>
-void launch_small(const SmallParams& p, bool fp8, hipStream_t stream) {
+void launch_small(const SmallParams& p, int mode, hipStream_t stream) {
     const size_t lds = small::lds_bytes(p.n, p.E);
-    if (fp8)
-        hipLaunchKernelGGL((layout_dispatch_small_kernel<VPL, true>), dim3(p.nwg), dim3(kThreads),
+    if (mode == 2)
+        hipLaunchKernelGGL((layout_dispatch_small_kernel<VPL, 2>), dim3(p.nwg), dim3(kThreads),
+                           lds, stream, p);
+    else if (mode == 1)
+        hipLaunchKernelGGL((layout_dispatch_small_kernel<VPL, 1>), dim3(p.nwg), dim3(kThreads),
                            lds, stream, p);
     else
-        hipLaunchKernelGGL((layout_dispatch_small_kernel<VPL, false>), dim3(p.nwg), dim3(kThreads),
+        hipLaunchKernelGGL((layout_dispatch_small_kernel<VPL, 0>), dim3(p.nwg), dim3(kThreads),
                            lds, stream, p);
 }
 
@@ -184,7 +195,7 @@ void launch_small(const SmallParams& p, bool fp8, hipStream_t stream) {
 
 hipError_t launch_layout_dispatch(const ep_problem& p, const int32_t* topk_idx,
                                   const ep_layout_t& out, void* workspace, const void* x,
-                                  void* recv_x, float* recv_scales, hipStream_t stream) {
+                                  void* recv_x, void* recv_scales, hipStream_t stream) {
     const int64_t n = static_cast<int64_t>(p.num_tokens) * p.num_topk;
     const int nvec = p.hidden / 8;
     // Few tokens: one piece per lane and more tiles, so that more groups run.

@@ -41,10 +41,10 @@ constexpr int64_t kFusedMaxVisits = int64_t{1} << 23;
 hipError_t launch_layout(const ep_problem& p, const int32_t* topk_idx, const ep_layout_t& out,
                          int32_t* workspace, hipStream_t stream);
 hipError_t launch_dispatch(const ep_problem& p, const void* x, const int32_t* slot_of,
-                           void* recv_x, float* recv_scales, hipStream_t stream);
+                           void* recv_x, void* recv_scales, hipStream_t stream);
 hipError_t launch_layout_dispatch(const ep_problem& p, const int32_t* topk_idx,
                                   const ep_layout_t& out, void* workspace, const void* x,
-                                  void* recv_x, float* recv_scales, hipStream_t stream);
+                                  void* recv_x, void* recv_scales, hipStream_t stream);
 hipError_t launch_combine(const ep_problem& p, const void* expert_out, const int32_t* slot_of,
                           const float* topk_weights, void* y, hipStream_t stream);
 hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);

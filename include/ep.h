@@ -85,7 +85,7 @@ enum {
 /* Shape of one dispatch / combine problem.  Host struct, read during the call
  * only.  Supported envelope: 0 <= T, 1 <= k <= 32, 1 <= E <= 1024, H >= 8 and
  * H % 8 == 0, H <= 65536, cap >= 0, T*k < 2^31, E*cap < 2^31, and H % 128 == 0
- * when use_fp8 = 1. */
+ * when use_fp8 != 0. */
 typedef struct ep_problem {
     int32_t num_tokens;   /* T */
     int32_t hidden;       /* H, channels per token */
@@ -94,7 +94,15 @@ typedef struct ep_problem {
     int32_t capacity;     /* 0: contiguous layout, rows grouped by expert, R = T*k.
                              > 0: fixed-capacity layout, expert e owns rows
                              [e*cap, (e+1)*cap), R = E*cap */
-    int32_t use_fp8;      /* 0: bf16 payload.  1: E4M3FN payload + fp32 scales */
+    int32_t use_fp8;      /* 0: bf16 payload.
+                             1: OCP E4M3FN payload, one fp32 scale per 128
+                                channels: scale = amax / 448, code = RNE(x / scale).
+                             2: E4M3FN payload, one UE8M0 scale byte per 128
+                                channels: the scale is 2^s for the smallest
+                                s >= -127 with 448 * 2^s >= amax, stored as the
+                                byte s + 127 (amax = 0: byte 0, codes 0).  The
+                                format is named in "[PR #206] [MERGED] Support
+                                UE8M0 data format"; the scale rule is a reading. */
 } ep_problem;
 
 /* Layout arrays, all int32 in device memory, written by ep_layout and read by
@@ -138,13 +146,14 @@ int ep_layout(const ep_problem* prob, const int32_t* topk_idx, const ep_layout_t
  * receive row slot.
  *   x            bf16 [T, H], device.
  *   layout       as written by ep_layout for the same problem (slot_of is read).
- *   recv_x       use_fp8 = 0: bf16 [R, H].  use_fp8 = 1: E4M3FN bytes [R, H].
- *   recv_scales  use_fp8 = 1: fp32 [R, H/128], the block scales of each row.
- *                Ignored (may be NULL) when use_fp8 = 0.
+ *   recv_x       use_fp8 = 0: bf16 [R, H].  use_fp8 = 1, 2: E4M3FN bytes [R, H].
+ *   recv_scales  the block scales of each row: use_fp8 = 1: fp32 [R, H/128];
+ *                use_fp8 = 2: UE8M0 bytes [R, H/128].  Ignored (may be NULL)
+ *                when use_fp8 = 0.
  * Receive rows that no entry fills are not written.  Every copy of a token is
  * bit-identical.  x must be finite. */
 int ep_dispatch(const ep_problem* prob, const void* x, const ep_layout_t* layout,
-                void* recv_x, float* recv_scales, void* stream);
+                void* recv_x, void* recv_scales, void* stream);
 
 /* Layout and dispatch in one call, with the same results as ep_layout
  * followed by ep_dispatch (every output of both is written).  Arguments as
@@ -155,7 +164,7 @@ int ep_dispatch(const ep_problem* prob, const void* x, const ep_layout_t* layout
  * touched.  Larger tables run the ep_layout and ep_dispatch kernels in turn. */
 int ep_layout_dispatch(const ep_problem* prob, const int32_t* topk_idx, const ep_layout_t* out,
                        void* workspace, size_t workspace_bytes, const void* x, void* recv_x,
-                       float* recv_scales, void* stream);
+                       void* recv_scales, void* stream);
 
 /* Combine: y[t][c] = bf16_RNE( fixed-order fused multiply-add chain over
  * j = 0..k-1 with slot_of[t*k+j] >= 0 of topk_weights[t*k+j] *

@@ -52,11 +52,13 @@ BAD_PROBLEMS = [
     (ep.Problem(4, 256, 0, 8), ep.EP_ERR_ARG),
     (ep.Problem(4, 256, 2, 0), ep.EP_ERR_ARG),
     (ep.Problem(4, 256, 2, 8, capacity=-1), ep.EP_ERR_ARG),
-    (ep.Problem(4, 256, 2, 8, use_fp8=2), ep.EP_ERR_ARG),
+    (ep.Problem(4, 256, 2, 8, use_fp8=3), ep.EP_ERR_ARG),
+    (ep.Problem(4, 256, 2, 8, use_fp8=-1), ep.EP_ERR_ARG),
     (ep.Problem(4, 256, 2, 1025), ep.EP_ERR_UNSUPPORTED),
     (ep.Problem(4, 256, 33, 8), ep.EP_ERR_UNSUPPORTED),
     (ep.Problem(4, 260, 2, 8), ep.EP_ERR_UNSUPPORTED),
     (ep.Problem(4, 72, 2, 8, use_fp8=1), ep.EP_ERR_UNSUPPORTED),
+    (ep.Problem(4, 72, 2, 8, use_fp8=2), ep.EP_ERR_UNSUPPORTED),
     (ep.Problem(4, 65544, 2, 8), ep.EP_ERR_UNSUPPORTED),
     (ep.Problem(1 << 28, 256, 8, 8), ep.EP_ERR_UNSUPPORTED),
     (ep.Problem(4, 256, 2, 1024, capacity=1 << 21), ep.EP_ERR_UNSUPPORTED),

@@ -33,7 +33,8 @@ def host_u16(t):
 
 class Case:
     def __init__(self, T, H, k, E, cap, fp8, x, idx, w, eo, name="case"):
-        self.T, self.H, self.k, self.E, self.cap, self.fp8 = T, H, k, E, cap, bool(fp8)
+        # fp8: 0 bf16 payload, 1 E4M3FN + fp32 scales, 2 E4M3FN + UE8M0 scales
+        self.T, self.H, self.k, self.E, self.cap, self.fp8 = T, H, k, E, cap, int(fp8)
         self.x, self.idx, self.w, self.eo, self.name = x, idx, w, eo, name
 
     @property
@@ -103,7 +104,7 @@ def check_case(c, got, tokens=None):
     # rows no entry fills keep the 0xFF sentinel (payload and scales)
     assert (got["recv_x"][~placed] == 0xFF).all(), f"{c.name}: unused receive rows written"
     if c.fp8:
-        assert (got["recv_s"][~placed].view(np.uint32) == 0xFFFFFFFF).all()
+        assert (got["recv_s"][~placed].view(np.uint8) == 0xFF).all(), f"{c.name}: unused scale rows written"
     if c.T == 0:
         return 1.0
     tok = np.arange(c.T) if tokens is None else np.asarray(tokens)
@@ -113,13 +114,13 @@ def check_case(c, got, tokens=None):
     compact[s_sel >= 0] = np.arange(len(rows), dtype=np.int32)
     x_sel = np.ascontiguousarray(c.x[tok])
     if c.fp8:
-        rx, rs = oracle.dispatch(x_sel, compact, len(rows), True)
+        rx, rs = oracle.dispatch(x_sel, compact, len(rows), c.fp8)
     else:
         rx, _ = oracle.dispatch(x_sel, compact, len(rows), False)
         rx = rx.view(np.uint8)
     np.testing.assert_array_equal(got["recv_x"][rows], rx, err_msg=f"{c.name}: payload")
     if c.fp8:
-        np.testing.assert_array_equal(got["recv_s"][rows].view(np.uint32), rs.view(np.uint32),
+        np.testing.assert_array_equal(got["recv_s"][rows].view(np.uint8), rs.view(np.uint8),
                                       err_msg=f"{c.name}: scales")
     ry, racc = oracle.combine(c.eo, s_sel, np.ascontiguousarray(c.w[tok]))
     gy = got["y"][tok]
@@ -310,6 +311,67 @@ def test_fp8_near_midpoint_quotients(fused):
     eo = workloads.to_bf16_bits(rng.standard_normal((T * k, H)).astype(np.float32))
     c = Case(T, H, k, E, 0, True, x, ids, w, eo, name="fp8_near_midpoint")
     check_case(c, run_gpu(c, fused=fused))
+
+
+# ---------------------------------------------------------------------------
+# UE8M0 scales (use_fp8 = 2)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+@pytest.mark.parametrize("cid", [2, 4])
+def test_ue8m0_workloads(cid, fused):
+    """The decode and skewed workloads with UE8M0 block scales."""
+    wl = workloads.make(cid)
+    c = Case.from_workload(wl)
+    c.fp8 = 2
+    c.name = wl.name + "_ue8m0"
+    check_case(c, run_gpu(c, fused=fused))
+
+
+def test_ue8m0_large_prefill_sampled():
+    c = Case.from_workload(workloads.make(5), nan_unused=False)
+    c.fp8 = 2
+    c.name = "large_prefill_ue8m0"
+    got = run_gpu(c)
+    rng = np.random.default_rng(5)
+    tok = np.unique(np.concatenate([[0, c.T - 1], rng.choice(c.T, 254, replace=False)]))
+    check_case(c, got, tokens=tok)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+def test_ue8m0_special_blocks(fused):
+    """Block maxima at exactly 448*2^j and one bf16 step either side of it,
+    bf16-subnormal blocks (exponent clamped at -127), zero and -0 blocks,
+    x100 outliers, with ragged tails and capacity overflow."""
+    rng = np.random.default_rng(41)
+    T, H, E, k = 40, 896, 6, 3
+    xf = (rng.standard_normal((T, H)) * 2.0 ** rng.integers(-40, 40, size=(T, 1))).astype(np.float32)
+    for t in range(T):
+        for b in range(H // 128):
+            sl = slice(128 * b, 128 * b + 128)
+            kind = (t * 7 + b) % 7
+            j = int(rng.integers(-110, 110))
+            if kind in (0, 1, 2):
+                base = np.float32(448.0 * 2.0 ** j).view(np.uint32)
+                amax = (base + np.uint32((kind == 1) << 16) - np.uint32((kind == 2) << 16)).view(np.float32)
+                xf[t, sl] = np.clip(xf[t, sl], -amax * 0.99, amax * 0.99)
+                xf[t, 128 * b + int(rng.integers(128))] = amax * rng.choice([-1, 1])
+            elif kind == 3:
+                xf[t, sl] = ((rng.integers(1, 128, 128).astype(np.uint32) << 16).view(np.float32)
+                             * rng.choice(np.float32([-1, 1]), 128))
+            elif kind == 4:
+                xf[t, sl] = -0.0 if t % 2 else 0.0
+            elif kind == 5:
+                xf[t, sl] *= 100.0
+    x = workloads.to_bf16_bits(xf)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    for cap in (0, 9):
+        R = T * k if cap == 0 else E * cap
+        eo = workloads.to_bf16_bits(rng.standard_normal((R, H)).astype(np.float32))
+        c = Case(T, H, k, E, cap, 2, x, ids, w, eo, name=f"ue8m0_special_cap{cap}")
+        c.nan_unused_rows()
+        check_case(c, run_gpu(c, fused=fused))
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
