@@ -33,13 +33,14 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "dispatch+combine effective GB/s and µs/call, % of HBM peak, 1×MI355X"
 
 
-def algorithmic_bytes(wl, count=None):
+def algorithmic_bytes(wl, count=None, scale_bytes=4):
     """Bytes the method must move (each input read once, each output written
-    once), per call.  V = routing entries that get a receive row."""
+    once), per call.  V = routing entries that get a receive row; scale_bytes
+    = 4 for fp32 block scales, 1 for UE8M0."""
     T, H, k, E = wl.T, wl.H, wl.k, wl.E
     V = T * k if count is None else int(sum(min(c, wl.cap) if wl.cap else c for c in count))
     p = 1 if wl.fp8 else 2
-    scales = 4 * V * (H // 128) if wl.fp8 else 0
+    scales = scale_bytes * V * (H // 128) if wl.fp8 else 0
     R = T * k if wl.cap == 0 else E * wl.cap
     layout_k = 4 * T * k + 4 * T * k + 4 * R + 4 * (2 * E + 1) + 8
     dispatch_k = 2 * T * H + 4 * T * k + V * H * p + scales
@@ -143,14 +144,14 @@ def measure_copy_gbps(torch, nbytes=1 << 30, reps=10):
     return 2 * nbytes / t / 1e9
 
 
-def cpu_baseline(wl, eo_host, bytes_total, target_s):
+def cpu_baseline(wl, eo_host, bytes_total, target_s, fp8_mode):
     import oracle
     reps, elapsed = 0, 0.0
     t_start = time.perf_counter()
     while reps < 2 or (elapsed < target_s and reps < 50):
         t0 = time.perf_counter()
         lay = oracle.layout(wl.topk_idx, wl.E, wl.cap)
-        oracle.dispatch(wl.x, lay["slot_of"], wl.R, wl.fp8)
+        oracle.dispatch(wl.x, lay["slot_of"], wl.R, fp8_mode)
         oracle.combine(eo_host, lay["slot_of"], wl.topk_weights, want_acc=False)
         elapsed += time.perf_counter() - t0
         reps += 1
@@ -171,6 +172,8 @@ def main():
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--scales", choices=["fp32", "ue8m0"], default="fp32",
+                    help="block-scale format of the FP8 workloads (2, 4, 5)")
     ap.add_argument("--path", choices=["separate", "fused"], default="separate",
                     help="separate: ep_layout then ep_dispatch; fused: ep_layout_dispatch")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -205,7 +208,8 @@ def main():
     wl = workloads.make(args.config)
     eo_host = wl.expert_out()
     dev = "cuda"
-    prob = ep.Problem(wl.T, wl.H, wl.k, wl.E, wl.cap, wl.fp8)
+    ue8m0 = bool(wl.fp8) and args.scales == "ue8m0"
+    prob = ep.Problem(wl.T, wl.H, wl.k, wl.E, wl.cap, 2 if ue8m0 else int(wl.fp8))
     idx = torch.from_numpy(wl.topk_idx).to(dev)
     w = torch.from_numpy(wl.topk_weights).to(dev)
     x = torch.from_numpy(wl.x.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -235,7 +239,7 @@ def main():
         step()
     torch.cuda.synchronize()
     count = lay.count.cpu().numpy()
-    nb = algorithmic_bytes(wl, count)
+    nb = algorithmic_bytes(wl, count, scale_bytes=1 if ue8m0 else 4)
 
     K = args.steps
     sh = stream.cuda_stream
@@ -287,7 +291,7 @@ def main():
     dom = max(kernels, key=lambda n: kernels[n][0])
     dom_ms, dom_bytes, dom_src = kernels[dom]
     achieved = dom_bytes / (dom_ms / 1e3) / 1e9
-    traffic = read_traffic(dom, dom_src, wl.name)
+    traffic = read_traffic(dom, dom_src, wl.name + ("_ue8m0" if ue8m0 else ""))
 
     copy_gbps = measure_copy_gbps(torch)
 
@@ -302,11 +306,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3" if wl.fp8 else "bf16",
+        "dtype": ("fp8e4m3+ue8m0" if ue8m0 else "fp8e4m3") if wl.fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "tokens": wl.T, "hidden": wl.H, "experts": wl.E,
                    "topk": wl.k, "capacity": wl.cap,
-                   "payload": "e4m3" if wl.fp8 else "bf16", "seed": wl.seed,
+                   "payload": "e4m3" if wl.fp8 else "bf16",
+                   "scales": ("ue8m0" if ue8m0 else "fp32") if wl.fp8 else None, "seed": wl.seed,
                    "routing": {1: "uniform distinct", 2: "uniform distinct",
                                3: "group-limited 8x32 top-4 groups",
                                4: "Zipf 1.2 without replacement",
@@ -336,7 +341,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, eo_host, total_bytes, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, eo_host, total_bytes, args.cpu_seconds,
+                                           prob.use_fp8)
     else:
         out["cpu_baseline"] = None
     ev.close()
