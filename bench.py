@@ -2,21 +2,24 @@
 """Benchmark of the MoE dispatch / combine hot path on one MI355X.
 
 One step = one pass of the whole path over one batch: ep_layout (routing
-layout, two kernels), ep_dispatch (scatter, one kernel) and ep_combine
-(gather-reduce, one kernel), on the 4096-token prefill workload: T=4096,
-H=7168, E=256 experts, top-8 group-limited routing (8 groups of 32, top-4
-groups), bf16 payload, contiguous layout, seed 0.  Inputs are synthetic,
-seeded, and already resident in HBM when the timed region starts.
+layout), ep_dispatch (scatter) and ep_combine (gather-reduce) -- or, with
+--path fused, ep_layout_dispatch and ep_combine -- by default on the
+4096-token prefill workload: T=4096, H=7168, E=256 experts, top-8
+group-limited routing (8 groups of 32, top-4 groups), bf16 payload,
+contiguous layout, seed 0.  Inputs are synthetic, seeded, and already
+resident in HBM when the timed region starts.
 
 Prints one JSON line.  `value` is effective GB/s of the whole step:
 algorithmic bytes of dispatch (layout included) plus combine, divided by the
 wall time per step of K back-to-back steps between two device
 synchronisations.  `roofline` reports the dominant kernel against the 8 TB/s
 HBM peak, with its duration measured by HIP events recorded around each
-kernel call on the stream it runs on, over a second run of K steps.  `cpu_baseline` times the CPU oracle
-on the same inputs (serial, one core).
+call on the stream it runs on, over a second run of K steps.
+`cpu_baseline` times the CPU oracle on the same inputs (serial, one core).
+--sweep skew instead prints one line per routing-skew variant.
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 3]
+                  [--path separate|fused] [--scales fp32|ue8m0] [--sweep skew]
                   [--no-cpu-baseline] [--cpu-seconds 12] [--copy-calibration]
 """
 import argparse
@@ -164,6 +167,121 @@ def cpu_baseline(wl, eo_host, bytes_total, target_s, fp8_mode):
                       f"serial C++ oracle, {per * 1e3:.1f} ms per pass"}
 
 
+def one_launch(wl):
+    """Whether ep_layout_dispatch takes this problem in its one-kernel form
+    (the library's own rule: at most 8192 routing entries and 2^23 id visits
+    over all workgroups)."""
+    n = wl.T * wl.k
+    nvec = wl.H // 8
+    vpl = 1 if wl.T < 1024 else (8 if nvec >= 1024 else (nvec + 127) // 128)
+    tiles = (nvec + 128 * vpl - 1) // (128 * vpl)
+    nwg = max(1, (wl.T * tiles + 1) // 2)
+    return n <= 8192 and n * nwg <= (1 << 23)
+
+
+def run_steps(ep, torch, wl, eo_host, prob, fused, K, W):
+    """W warm-up steps, then two timed loops of K steps: an event-free one
+    (wall time per step) and one with HIP events around every call on the
+    kernels' stream (per-call durations)."""
+    import numpy as np
+    dev = "cuda"
+    idx = torch.from_numpy(wl.topk_idx).to(dev)
+    w = torch.from_numpy(wl.topk_weights).to(dev)
+    x = torch.from_numpy(wl.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    eo = torch.from_numpy(eo_host.view(np.int16)).to(dev).view(torch.bfloat16)
+    lay = ep.Layout.empty(prob, dev)
+    ws = ep.alloc_workspace(prob, dev)
+    recv_x, recv_s = ep.alloc_recv(prob, dev)
+    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
+    if fused:
+        # one call does both; the layout bracket below is left empty
+        do_layout = lambda s: None  # noqa: E731
+        do_dispatch = ep.prepare_layout_dispatch(prob, idx, lay, ws, x, recv_x, recv_s)
+    else:
+        do_layout = ep.prepare_layout(prob, idx, lay, ws)
+        do_dispatch = ep.prepare_dispatch(prob, x, lay, recv_x, recv_s)
+    do_combine = ep.prepare_combine(prob, eo, lay, w, y)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        do_layout(stream)
+        do_dispatch(stream)
+        do_combine(stream)
+
+    print(f"[bench] warmup {W} steps", file=sys.stderr, flush=True)
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    count = lay.count.cpu().numpy()
+    sh = stream.cuda_stream
+
+    # Timed region 1: K steps back to back, nothing between the kernels.
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"[bench] timed {K} steps in {wall:.4f} s", file=sys.stderr, flush=True)
+
+    # Timed region 2: the same K steps with a HIP event before and after every
+    # call on the kernels' stream.  The events add a small bubble between
+    # kernels, which is why region 1 gives the step time.
+    ev = HipEvents(4 * K)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(K):
+        ev.record(4 * i, sh)
+        do_layout(stream)
+        ev.record(4 * i + 1, sh)
+        do_dispatch(stream)
+        ev.record(4 * i + 2, sh)
+        do_combine(stream)
+        ev.record(4 * i + 3, sh)
+    torch.cuda.synchronize()
+    wall_events = time.perf_counter() - t1
+
+    def mean_ms(a, b):
+        return sum(ev.elapsed_ms(4 * i + a, 4 * i + b) for i in range(K)) / K
+
+    out = dict(count=count, wall=wall, wall_events=wall_events, layout_ms=mean_ms(0, 1),
+               dispatch_ms=mean_ms(1, 2), combine_ms=mean_ms(2, 3))
+    ev.close()
+    return out
+
+
+def skew_sweep(ep, torch, workloads, args):
+    """Sensitivity of the step to routing skew: the 4096-token prefill shape
+    with 16 hot experts at 1.0-3.0x the mean load, and the skewed shape with
+    Zipf exponents 0.8, 1.2, 1.6.  One JSON line per variant."""
+    import numpy as np
+    variants = [(3, dict(), "hot 1.0x")] + \
+        [(3, dict(hot_experts=16, hot_ratio=r), f"hot {r}x") for r in (1.5, 2.0, 3.0)] + \
+        [(4, dict(zipf_s=s), f"zipf {s}") for s in (0.8, 1.2, 1.6)]
+    for cid, over, label in variants:
+        wl = workloads.make(cid, **over)
+        eo_host = wl.expert_out()
+        prob = ep.Problem(wl.T, wl.H, wl.k, wl.E, wl.cap, int(wl.fp8))
+        r = run_steps(ep, torch, wl, eo_host, prob, False, args.steps, args.warmup)
+        nb = algorithmic_bytes(wl, r["count"])
+        ms = r["wall"] / args.steps * 1e3
+        total = nb["dispatch_total"] + nb["combine_total"]
+        counts = np.asarray(r["count"])
+        print(json.dumps({
+            "metric": METRIC, "sweep": "skew", "variant": label,
+            "value": round(total / (ms / 1e3) / 1e9, 2), "unit": "GB/s",
+            "ms_per_step": round(ms, 5), "pct_of_hbm_peak": round(100 * total / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 2),
+            "config": {"workload": wl.name, "tokens": wl.T, "hidden": wl.H, "experts": wl.E,
+                       "topk": wl.k, "payload": "e4m3" if wl.fp8 else "bf16", **over,
+                       "hot_load_ratio": wl.meta.get("hot_load_ratio")},
+            "max_over_mean_expert_load": round(float(counts.max() / counts.mean()), 3),
+            "us_per_call": {"layout": round(r["layout_ms"] * 1e3, 3),
+                            "dispatch": round(r["dispatch_ms"] * 1e3, 3),
+                            "combine": round(r["combine_ms"] * 1e3, 3)},
+        }), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +290,9 @@ def main():
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--sweep", choices=["skew"], default=None,
+                    help="skew: routing-skew sensitivity (one JSON line per variant) instead "
+                         "of the single benchmark line")
     ap.add_argument("--scales", choices=["fp32", "ue8m0"], default="fp32",
                     help="block-scale format of the FP8 workloads (2, 4, 5)")
     ap.add_argument("--path", choices=["separate", "fused"], default="separate",
@@ -204,84 +325,26 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": a.numel()}))
         return 0
+    if args.sweep == "skew":
+        return skew_sweep(ep, torch, workloads, args)
+
     print(f"[bench] generating workload {args.config}", file=sys.stderr, flush=True)
     wl = workloads.make(args.config)
     eo_host = wl.expert_out()
-    dev = "cuda"
     ue8m0 = bool(wl.fp8) and args.scales == "ue8m0"
     prob = ep.Problem(wl.T, wl.H, wl.k, wl.E, wl.cap, 2 if ue8m0 else int(wl.fp8))
-    idx = torch.from_numpy(wl.topk_idx).to(dev)
-    w = torch.from_numpy(wl.topk_weights).to(dev)
-    x = torch.from_numpy(wl.x.view(np.int16)).to(dev).view(torch.bfloat16)
-    eo = torch.from_numpy(eo_host.view(np.int16)).to(dev).view(torch.bfloat16)
-    lay = ep.Layout.empty(prob, dev)
-    ws = ep.alloc_workspace(prob, dev)
-    recv_x, recv_s = ep.alloc_recv(prob, dev)
-    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
     fused = args.path == "fused"
-    if fused:
-        # one call does both; the layout bracket below is left empty
-        do_layout = lambda s: None  # noqa: E731
-        do_dispatch = ep.prepare_layout_dispatch(prob, idx, lay, ws, x, recv_x, recv_s)
-    else:
-        do_layout = ep.prepare_layout(prob, idx, lay, ws)
-        do_dispatch = ep.prepare_dispatch(prob, x, lay, recv_x, recv_s)
-    do_combine = ep.prepare_combine(prob, eo, lay, w, y)
-    stream = torch.cuda.current_stream()
-
-    def step():
-        do_layout(stream)
-        do_dispatch(stream)
-        do_combine(stream)
-
-    print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    count = lay.count.cpu().numpy()
-    nb = algorithmic_bytes(wl, count, scale_bytes=1 if ue8m0 else 4)
-
+    r = run_steps(ep, torch, wl, eo_host, prob, fused, args.steps, args.warmup)
+    nb = algorithmic_bytes(wl, r["count"], scale_bytes=1 if ue8m0 else 4)
     K = args.steps
-    sh = stream.cuda_stream
-
-    # Timed region 1: K steps back to back, nothing between the kernels.
-    # `value` and `ms_per_step` come from here.
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    print(f"[bench] timed {K} steps in {wall:.4f} s", file=sys.stderr, flush=True)
-
-    # Timed region 2: the same K steps with a HIP event before and after every
-    # kernel call on the kernels' stream; per-kernel durations (and the
-    # roofline) come from here.  The events themselves add a small bubble
-    # between kernels, which is why region 1 gives the step time.
-    ev = HipEvents(4 * K)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for i in range(K):
-        ev.record(4 * i, sh)
-        do_layout(stream)
-        ev.record(4 * i + 1, sh)
-        do_dispatch(stream)
-        ev.record(4 * i + 2, sh)
-        do_combine(stream)
-        ev.record(4 * i + 3, sh)
-    torch.cuda.synchronize()
-    wall_events = time.perf_counter() - t1
-
-    def mean_ms(a, b):
-        return sum(ev.elapsed_ms(4 * i + a, 4 * i + b) for i in range(K)) / K
-
-    layout_ms, dispatch_ms, combine_ms = mean_ms(0, 1), mean_ms(1, 2), mean_ms(2, 3)
+    wall, wall_events = r["wall"], r["wall_events"]
+    layout_ms, dispatch_ms, combine_ms = r["layout_ms"], r["dispatch_ms"], r["combine_ms"]
     ms_per_step = wall / K * 1e3
     total_bytes = nb["dispatch_total"] + nb["combine_total"]
     value = total_bytes / (ms_per_step / 1e3) / 1e9
 
-    if fused:
-        disp_entry = ("layout_dispatch_kernel",
+    if fused and one_launch(wl):
+        disp_entry = ("layout_dispatch_small_kernel",
                       (dispatch_ms, nb["dispatch_kernel"] + nb["layout_kernels"], "ep_fused.hip"))
     else:
         disp_entry = ("dispatch_bf16_kernel" if not wl.fp8 else "dispatch_fp8_kernel",
@@ -345,7 +408,6 @@ def main():
                                            prob.use_fp8)
     else:
         out["cpu_baseline"] = None
-    ev.close()
     print(json.dumps(out), flush=True)
     return 0
 

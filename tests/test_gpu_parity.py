@@ -313,6 +313,17 @@ def test_fp8_near_midpoint_quotients(fused):
     check_case(c, run_gpu(c, fused=fused))
 
 
+@pytest.mark.parametrize("over", [dict(cid=3, T=1024, hot_experts=16, hot_ratio=3.0),
+                                  dict(cid=4, T=2048, zipf_s=1.6),
+                                  dict(cid=4, T=2048, zipf_s=0.8)],
+                         ids=["hot3x", "zipf1.6", "zipf0.8"])
+def test_skew_sweep_variants(over):
+    """The routing-skew sweep's extreme variants, at reduced token counts."""
+    over = dict(over)
+    c = Case.from_workload(workloads.make(over.pop("cid"), **over))
+    check_case(c, run_gpu(c))
+
+
 # ---------------------------------------------------------------------------
 # UE8M0 scales (use_fp8 = 2)
 # ---------------------------------------------------------------------------

@@ -205,7 +205,8 @@ def make(cid, seed=0, **overrides):
         logits = rr.standard_normal((T, E), dtype=np.float32)
         if cfg.get("hot_experts"):
             hot = _rng(seed, cid, _HOT).permutation(E)[: cfg["hot_experts"]]
-            beta, r = _hot_bias(logits, hot, k, cfg["hot_ratio"], (seed, cid, T, E, k))
+            beta, r = _hot_bias(logits, hot, k, cfg["hot_ratio"],
+                                (seed, cid, T, E, k, len(hot), cfg["hot_ratio"]))
             logits[:, hot] += np.float32(beta)
             meta.update(hot_experts=np.sort(hot), hot_bias=beta, hot_load_ratio=r)
         idx = group_limited_topk(logits, k)
