@@ -1,10 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the MoE dispatch / combine hot path on one MI355X.
 
-One step = one pass of the whole path over one batch: ep_layout (routing
-layout), ep_dispatch (scatter) and ep_combine (gather-reduce) -- or, with
---path fused, ep_layout_dispatch and ep_combine -- by default on the
-4096-token prefill workload: T=4096, H=7168, E=256 experts, top-8
+One step = one pass of the whole path over one batch: ep_layout_dispatch
+(routing layout and scatter in one call) and ep_combine (gather-reduce) --
+or, with --path separate, ep_layout, ep_dispatch and ep_combine -- by
+default on the 4096-token prefill workload: T=4096, H=7168, E=256 experts, top-8
 group-limited routing (8 groups of 32, top-4 groups), bf16 payload,
 contiguous layout, seed 0.  Inputs are synthetic, seeded, and already
 resident in HBM when the timed region starts.
@@ -12,9 +12,10 @@ resident in HBM when the timed region starts.
 Prints one JSON line.  `value` is effective GB/s of the whole step:
 algorithmic bytes of dispatch (layout included) plus combine, divided by the
 wall time per step of K back-to-back steps between two device
-synchronisations.  `roofline` reports the dominant kernel against the 8 TB/s
+synchronisations.  `roofline` reports the dominant call against the 8 TB/s
 HBM peak, with its duration measured by HIP events recorded around each
-call on the stream it runs on, over a second run of K steps.
+call on the stream it runs on, over a second run of K steps (a call of
+ep_layout_dispatch is one or two kernels: it is reported as a unit).
 `cpu_baseline` times the CPU oracle on the same inputs (serial, one core).
 --sweep skew instead prints one line per routing-skew variant.
 
@@ -55,11 +56,11 @@ def algorithmic_bytes(wl, count=None, scale_bytes=4):
                 combine_kernel=combine_k, dispatch_total=b_disp, combine_total=b_comb)
 
 
-def kernel_source_digest(name):
-    """Digest of a kernel source file and every csrc header it includes,
+def kernel_source_digest(*names):
+    """Digest of kernel source files and every csrc header they include,
     directly or not (quoted includes)."""
     csrc = os.path.join(ROOT, "combine_ep_layout_09_amd", "csrc")
-    seen, todo = [], [name]
+    seen, todo = [], list(names)
     while todo:
         f = todo.pop(0)
         if f in seen or not os.path.exists(os.path.join(csrc, f)):
@@ -75,10 +76,12 @@ def kernel_source_digest(name):
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel, source, workload):
+def read_traffic(kernel, sources, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}.txt")
+    was taken on the current kernel sources; else None."""
+    # several kernels of one ep_layout_dispatch call: one summary for the call
+    key = "ep_layout_dispatch" if "+" in kernel else kernel
+    path = os.path.join(ROOT, "profiles", f"pmc_{key}_{workload}.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -86,7 +89,7 @@ def read_traffic(kernel, source, workload):
         if ":" in line:
             key, _, v = line.partition(":")
             vals[key.strip()] = v.strip()
-    if vals.get("source_digest") != kernel_source_digest(source):
+    if vals.get("source_digest") != kernel_source_digest(*sources):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -179,6 +182,22 @@ def one_launch(wl):
     return n <= 8192 and n * nwg <= (1 << 23)
 
 
+# sources of every kernel an ep_layout_dispatch call may launch
+FUSED_SOURCES = ("ep_fused.hip", "ep_layout.hip", "ep_dispatch.hip")
+
+
+def fused_call_name(wl):
+    """The kernels of one ep_layout_dispatch call on this workload (the
+    library's rule: one kernel for small tables; the histogram kernel and the
+    ranking dispatch kernel for bf16 rows or k >= 8; otherwise the layout
+    kernels and the dispatch kernel)."""
+    if one_launch(wl):
+        return "layout_dispatch_small_kernel"
+    if not wl.fp8 or wl.k >= 8:
+        return "layout_hist_kernel+layout_dispatch_ranked_kernel"
+    return "layout_hist_kernel+layout_rank_kernel+dispatch_fp8_kernel"
+
+
 def run_steps(ep, torch, wl, eo_host, prob, fused, K, W):
     """W warm-up steps, then two timed loops of K steps: an event-free one
     (wall time per step) and one with HIP events around every call on the
@@ -262,13 +281,14 @@ def skew_sweep(ep, torch, workloads, args):
         wl = workloads.make(cid, **over)
         eo_host = wl.expert_out()
         prob = ep.Problem(wl.T, wl.H, wl.k, wl.E, wl.cap, int(wl.fp8))
-        r = run_steps(ep, torch, wl, eo_host, prob, False, args.steps, args.warmup)
+        r = run_steps(ep, torch, wl, eo_host, prob, args.path == "fused", args.steps,
+                      args.warmup)
         nb = algorithmic_bytes(wl, r["count"])
         ms = r["wall"] / args.steps * 1e3
         total = nb["dispatch_total"] + nb["combine_total"]
         counts = np.asarray(r["count"])
         print(json.dumps({
-            "metric": METRIC, "sweep": "skew", "variant": label,
+            "metric": METRIC, "sweep": "skew", "variant": label, "path": args.path,
             "value": round(total / (ms / 1e3) / 1e9, 2), "unit": "GB/s",
             "ms_per_step": round(ms, 5), "pct_of_hbm_peak": round(100 * total / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 2),
             "config": {"workload": wl.name, "tokens": wl.T, "hidden": wl.H, "experts": wl.E,
@@ -295,8 +315,8 @@ def main():
                          "of the single benchmark line")
     ap.add_argument("--scales", choices=["fp32", "ue8m0"], default="fp32",
                     help="block-scale format of the FP8 workloads (2, 4, 5)")
-    ap.add_argument("--path", choices=["separate", "fused"], default="separate",
-                    help="separate: ep_layout then ep_dispatch; fused: ep_layout_dispatch")
+    ap.add_argument("--path", choices=["separate", "fused"], default="fused",
+                    help="fused: ep_layout_dispatch; separate: ep_layout then ep_dispatch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run one device-to-device copy of 256 MiB (for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -343,14 +363,16 @@ def main():
     total_bytes = nb["dispatch_total"] + nb["combine_total"]
     value = total_bytes / (ms_per_step / 1e3) / 1e9
 
-    if fused and one_launch(wl):
-        disp_entry = ("layout_dispatch_small_kernel",
-                      (dispatch_ms, nb["dispatch_kernel"] + nb["layout_kernels"], "ep_fused.hip"))
+    if fused:
+        # the whole ep_layout_dispatch call: the layout's and the dispatch's
+        # algorithmic bytes, over the call's duration
+        disp_entry = (fused_call_name(wl),
+                      (dispatch_ms, nb["dispatch_total"], FUSED_SOURCES))
     else:
         disp_entry = ("dispatch_bf16_kernel" if not wl.fp8 else "dispatch_fp8_kernel",
-                      (dispatch_ms, nb["dispatch_kernel"], "ep_dispatch.hip"))
+                      (dispatch_ms, nb["dispatch_kernel"], ("ep_dispatch.hip",)))
     kernels = {disp_entry[0]: disp_entry[1],
-               "combine_kernel": (combine_ms, nb["combine_kernel"], "ep_combine.hip")}
+               "combine_kernel": (combine_ms, nb["combine_kernel"], ("ep_combine.hip",))}
     dom = max(kernels, key=lambda n: kernels[n][0])
     dom_ms, dom_bytes, dom_src = kernels[dom]
     achieved = dom_bytes / (dom_ms / 1e3) / 1e9

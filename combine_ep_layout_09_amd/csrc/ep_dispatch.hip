@@ -87,18 +87,11 @@ TileShape row_tile_shape(int nvec, int vpl) {
     return {((per_tile + 63) / 64) * 64, tiles};
 }
 
-namespace {
-
 // For batches of 1024 tokens or more, bf16 dispatch tiles are two waves wide
 // with up to eight 16-byte pieces per lane, so one workgroup covers a whole
 // row of up to 1024 pieces (H = 8192); FP8 tiles have two pieces per lane and
 // as many lanes as the row needs (up to 1024).  The pieces of a lane are all
 // loaded before the first store.
-struct DispatchShape {
-    int vpl;
-    TileShape tile;
-};
-
 DispatchShape dispatch_shape(int nvec, int T, bool fp8) {
     // Few tokens (decode batches): wide workgroups, one piece per lane, so
     // that enough waves exist to keep HBM busy.
@@ -110,6 +103,8 @@ DispatchShape dispatch_shape(int nvec, int T, bool fp8) {
     const int vpl = two_wave_vpl(nvec);
     return {vpl, {128, (nvec + 128 * vpl - 1) / (128 * vpl)}};
 }
+
+namespace {
 
 template <int VPL>
 void launch_vpl(const ep_problem& p, dim3 grid, int threads, const void* x, int nvec,

@@ -20,6 +20,14 @@ struct TileShape {
 };
 TileShape row_tile_shape(int nvec, int vpl);
 
+// Dispatch launch shape: pieces per lane and the (token, column tile) grid's
+// tile width and count.
+struct DispatchShape {
+    int vpl;
+    TileShape tile;
+};
+DispatchShape dispatch_shape(int nvec, int T, bool fp8);
+
 // Partition of the T*k routing entries into layout blocks.
 struct LayoutGeometry {
     int64_t entries;   // T*k
@@ -40,6 +48,12 @@ constexpr int64_t kFusedMaxVisits = int64_t{1} << 23;
 
 hipError_t launch_layout(const ep_problem& p, const int32_t* topk_idx, const ep_layout_t& out,
                          int32_t* workspace, hipStream_t stream);
+// The histogram kernel alone, with the per-block expert prefixes the ranking
+// dispatch kernel of ep_layout_dispatch reads (two tables in the workspace);
+// also zeroes status[1].
+hipError_t launch_layout_tables(const ep_problem& p, const int32_t* topk_idx,
+                                const LayoutGeometry& g, int32_t* workspace, int32_t* status,
+                                hipStream_t stream);
 hipError_t launch_dispatch(const ep_problem& p, const void* x, const int32_t* slot_of,
                            void* recv_x, void* recv_scales, hipStream_t stream);
 hipError_t launch_layout_dispatch(const ep_problem& p, const int32_t* topk_idx,

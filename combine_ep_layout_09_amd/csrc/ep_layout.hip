@@ -92,11 +92,12 @@ __global__ __launch_bounds__(small::kThreads) void layout_small_kernel(
 
 // ---- two-pass path -----------------------------------------------------------
 
+template <bool PREFIX>
 __global__ __launch_bounds__(kHistThreads) void layout_hist_kernel(
         const int32_t* __restrict__ idx, int64_t n, int E, int chunk, int nblocks,
-        int32_t* __restrict__ block_hist) {
+        int32_t* __restrict__ block_hist, int32_t* __restrict__ status) {
     extern __shared__ int32_t hist[];  // [E + 1]; hist[E] counts invalid ids
-    hist_block(blockIdx.x, hist, idx, n, E, chunk, nblocks, block_hist);
+    hist_block<PREFIX>(blockIdx.x, hist, idx, n, E, chunk, nblocks, block_hist, status);
 }
 
 __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
@@ -135,9 +136,20 @@ LayoutGeometry layout_geometry_two_pass(const ep_problem& p) {
 }
 
 int64_t layout_workspace_bytes(const ep_problem& p) {
-    // the block-histogram table of the two-pass path
-    const int64_t bytes = static_cast<int64_t>(kTableStride) * (p.num_experts + 1) * 4;
+    // the block-histogram table of the two-pass path, and the table of
+    // per-block expert prefixes that the ranking dispatch kernel reads
+    const int64_t bytes = 2 * static_cast<int64_t>(kTableStride) * (p.num_experts + 1) * 4;
     return ((bytes + 255) / 256) * 256;
+}
+
+hipError_t launch_layout_tables(const ep_problem& p, const int32_t* topk_idx,
+                                const LayoutGeometry& g, int32_t* workspace, int32_t* status,
+                                hipStream_t stream) {
+    const size_t lds_hist = static_cast<size_t>(p.num_experts + 1) * 4;
+    hipLaunchKernelGGL(layout_hist_kernel<true>, dim3(g.blocks), dim3(kHistThreads), lds_hist,
+                       stream, topk_idx, g.entries, p.num_experts, g.chunk, g.blocks, workspace,
+                       status);
+    return hipGetLastError();
 }
 
 hipError_t launch_layout(const ep_problem& p, const int32_t* topk_idx, const ep_layout_t& out,
@@ -155,8 +167,8 @@ hipError_t launch_layout(const ep_problem& p, const int32_t* topk_idx, const ep_
         return hipGetLastError();
     }
     const size_t lds_hist = static_cast<size_t>(E + 1) * 4;
-    hipLaunchKernelGGL(layout_hist_kernel, dim3(g.blocks), dim3(kHistThreads), lds_hist, stream,
-                       topk_idx, g.entries, E, g.chunk, g.blocks, block_hist);
+    hipLaunchKernelGGL(layout_hist_kernel<false>, dim3(g.blocks), dim3(kHistThreads), lds_hist,
+                       stream, topk_idx, g.entries, E, g.chunk, g.blocks, block_hist, nullptr);
     hipLaunchKernelGGL(layout_rank_kernel, dim3(g.blocks), dim3(kRankThreads), rank_lds_bytes(E),
                        stream, topk_idx, g.entries, E, p.capacity, g.chunk, g.blocks, R,
                        block_hist, out.count, out.offset, out.slot_of, out.src_of_slot,

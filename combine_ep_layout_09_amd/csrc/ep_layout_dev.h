@@ -284,8 +284,14 @@ __device__ __forceinline__ int4 load_group(const int32_t* __restrict__ idx, int6
 // Histogram of block b's entries, stored as column entries b of the
 // block-histogram table (the whole workgroup, kHistThreads wide, calls it;
 // hist is LDS of E+1 words; the last block zeroes the table's padding).
+// PREFIX: also the exclusive scan of the block's valid counts over experts,
+// as column entries b of a second table of the same shape right after the
+// first (its column E holds the block's number of valid entries), and block
+// 0 zeroes status[1] for the dispatch kernel that ranks from these tables.
+template <bool PREFIX = false>
 __device__ void hist_block(int b, int32_t* hist, const int32_t* __restrict__ idx, int64_t n,
-                           int E, int chunk, int nblocks, int32_t* __restrict__ block_hist) {
+                           int E, int chunk, int nblocks, int32_t* __restrict__ block_hist,
+                           int32_t* __restrict__ status = nullptr) {
     for (int e = threadIdx.x; e <= E; e += kHistThreads) hist[e] = 0;
     __syncthreads();
 
@@ -319,6 +325,29 @@ __device__ void hist_block(int b, int32_t* hist, const int32_t* __restrict__ idx
         if (b == nblocks - 1)
             for (int p = nblocks; p < kTableStride; ++p)
                 block_hist[static_cast<int64_t>(e) * kTableStride + p] = 0;
+    }
+    if (PREFIX) {
+        int32_t* prefix = block_hist + static_cast<int64_t>(E + 1) * kTableStride;
+        if (b == 0 && threadIdx.x == 0) status[1] = 0;
+        if (threadIdx.x < kWave) {  // wave 0: each lane scans a run of experts
+            const uint32_t lane = lane_id();
+            const int per = (E + kWave - 1) / kWave;
+            const int e0 = min(E, static_cast<int>(lane) * per);
+            const int e1 = min(E, e0 + per);
+            int32_t local = 0;
+            for (int e = e0; e < e1; ++e) local += hist[e];
+            const int32_t incl = wave_inclusive_scan(local);
+            int32_t run = incl - local;
+            for (int e = e0; e < e1; ++e) {
+                prefix[static_cast<int64_t>(e) * kTableStride + b] = run;
+                run += hist[e];
+            }
+            if (lane == kWave - 1) prefix[static_cast<int64_t>(E) * kTableStride + b] = incl;
+        }
+        if (b == nblocks - 1)
+            for (int e = threadIdx.x; e <= E; e += kHistThreads)
+                for (int p = nblocks; p < kTableStride; ++p)
+                    prefix[static_cast<int64_t>(e) * kTableStride + p] = 0;
     }
 }
 

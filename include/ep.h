@@ -122,9 +122,9 @@ typedef struct ep_layout_t {
 int64_t ep_num_recv_rows(const ep_problem* prob);
 
 /* Bytes of device workspace ep_layout and ep_layout_dispatch need for this
- * problem (a multiple of 256: the block-histogram table of 64 * (E + 1)
- * int32), or -1 if the problem is invalid.  Its contents need no
- * initialisation and are scratch after the call. */
+ * problem (a multiple of 256: two tables of 64 * (E + 1) int32, per-block
+ * expert counts and their prefix sums), or -1 if the problem is invalid.
+ * Its contents need no initialisation and are scratch after the call. */
 int64_t ep_layout_workspace_bytes(const ep_problem* prob);
 
 /* Routing layout.
@@ -161,7 +161,13 @@ int ep_dispatch(const ep_problem* prob, const void* x, const ep_layout_t* layout
  * (T*k, decode-sized batches) it is one kernel launch in which no workgroup
  * waits for another: each one derives the slots of its own tokens from the
  * whole table while its rows load, then stores them; the workspace is not
- * touched.  Larger tables run the ep_layout and ep_dispatch kernels in turn. */
+ * touched.  Larger tables take two launches for bf16 payloads and for FP8
+ * with k >= 8: the layout's histogram kernel (which also writes per-block
+ * prefix sums over experts to the workspace), then a dispatch kernel in
+ * which each workgroup computes its own token's slots from those tables and
+ * the routing entries ahead of the token in its block before it moves the
+ * row; FP8 with k < 8 runs the ep_layout and ep_dispatch kernels in turn.
+ * Either way no workgroup waits for another. */
 int ep_layout_dispatch(const ep_problem* prob, const int32_t* topk_idx, const ep_layout_t* out,
                        void* workspace, size_t workspace_bytes, const void* x, void* recv_x,
                        void* recv_scales, void* stream);

@@ -201,6 +201,22 @@ EDGE = [
     dict(T=1024, H=256, k=8, E=16, cap=0, fp8=False, name="fused_largest_table"),
     dict(T=2730, H=128, k=3, E=2, cap=3000, fp8=True, name="fused_two_experts_capacity"),
     dict(T=3, H=8, k=5, E=1000, cap=2, fp8=False, name="fused_few_tokens_many_experts"),
+    # ep_layout_dispatch above 8192 entries with bf16 rows or FP8 and k >= 8:
+    # histogram tables, then a dispatch kernel that ranks each token's
+    # entries itself.  Tokens straddling layout blocks (k does not divide the
+    # block size), more entries than 16-lane rows in a workgroup, blocks wider
+    # than one pass over the ids, rows of two column tiles, few tokens with a
+    # wide k, one expert, capacity with overflow.
+    dict(T=3000, H=256, k=5, E=50, cap=0, fp8=False, name="ranked_odd_k_straddle"),
+    dict(T=1024, H=2048, k=16, E=128, cap=0, fp8=False, name="ranked_k16_two_rounds"),
+    dict(T=4500, H=3584, k=8, E=96, cap=0, fp8=False, name="ranked_wide_blocks_bf16"),
+    dict(T=1100, H=9216, k=8, E=64, cap=0, fp8=False, name="ranked_two_tiles_bf16"),
+    dict(T=600, H=1024, k=16, E=64, cap=0, fp8=True, name="ranked_few_tokens_k16"),
+    dict(T=9000, H=128, k=1, E=1, cap=0, fp8=False, name="ranked_one_expert"),
+    dict(T=1800, H=512, k=8, E=20, cap=700, fp8=True, name="ranked_capacity_overflow"),
+    dict(T=2300, H=256, k=6, E=20, cap=700, fp8=False, name="ranked_capacity_overflow_bf16_k6"),
+    # FP8 with k < 8 above 8192 entries: the layout kernels, then dispatch
+    dict(T=2300, H=512, k=6, E=20, cap=700, fp8=True, name="fp8_k6_capacity_overflow"),
 ]
 
 
@@ -225,6 +241,26 @@ def test_duplicate_and_invalid_ids():
     for cap, fp8, fused in ((0, False, False), (0, True, False), (40, True, False),
                             (0, False, True), (40, True, True)):
         c = _random_case(T, 256, k, E, cap, fp8, seed=cap, ids=ids, name=f"dup_invalid_cap{cap}")
+        got = run_gpu(c, fused=fused)
+        check_case(c, got)
+        assert got["status"][0] == int(((ids < 0) | (ids >= E)).sum())
+
+
+def test_duplicate_and_invalid_ids_large_table():
+    """The same id mix above 8192 entries (two-kernel layout; ranking inside
+    the dispatch kernel of ep_layout_dispatch), with and without capacity."""
+    rng = np.random.default_rng(10)
+    T, k, E = 2100, 8, 40
+    ids = rng.integers(0, E, size=(T, k))
+    ids[::7, 1] = ids[::7, 0]
+    ids[::11, 2] = -1
+    ids[::13, 3] = E
+    ids[::17, 0] = 1 << 30
+    ids[100:140] = 5                               # a run of one expert across tokens
+    for cap, fp8, fused in ((0, False, False), (0, False, True), (300, True, False),
+                            (300, True, True), (0, 2, True)):
+        c = _random_case(T, 256, k, E, cap, fp8, seed=cap + 1, ids=ids,
+                         name=f"dup_invalid_large_cap{cap}_fp8{int(fp8)}")
         got = run_gpu(c, fused=fused)
         check_case(c, got)
         assert got["status"][0] == int(((ids < 0) | (ids >= E)).sum())
@@ -395,8 +431,9 @@ def test_non_default_stream(fused):
 def test_fused_equals_separate_bitwise():
     """ep_layout_dispatch writes exactly what ep_layout + ep_dispatch write,
     receive rows and scales included, on the tiny and the decode workloads
-    (one-kernel path) and the skewed workload (two-kernel path)."""
-    for cid in (1, 2, 4):
+    (one-kernel path) and the prefill and skewed workloads (histogram kernel
+    plus ranking dispatch kernel)."""
+    for cid in (1, 2, 3, 4):
         c = Case.from_workload(workloads.make(cid))
         a = run_gpu(c)
         b = run_gpu(c, fused=True)
