@@ -112,11 +112,155 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(
     }
 }
 
+// ---- persistent form: every wave reads all its rows, then writes ----------
+//
+// HBM pays for switching between reads and writes; a combine whose 2TH bytes
+// of output stores are spread evenly through its 2VH bytes of row loads
+// runs well below the rate of the loads alone (measured: the prefill
+// combine's loads alone take about 70 us, its stores alone about 13 us,
+// interleaved about 93 us).  Here one 1024-lane workgroup per CU owns a
+// contiguous run of (token, 64-piece chunk) units per wave, computes up to
+// kHold of them into registers -- one chunk at a time per wave, since its
+// loads must not be hoisted into the held registers -- and only then stores
+// them.  Every wave does the same amount of work from the same start, so
+// the waves of the whole chip reach their store bursts at about the same
+// time, without any barrier.  Larger problems take one launch per kHold
+// chunks per wave, over consecutive token ranges: a kernel boundary keeps
+// each launch's read and write phases aligned across the chip, which waves
+// looping over rounds inside one launch do not stay (measured: 4 rounds in
+// one launch at the 16384-token prefill were 7% slower than the per-token
+// kernel).
+
+constexpr int kPersistThreads = 1024;
+constexpr int kPersistWaves = kPersistThreads / kWave;
+constexpr int kHold = 14;  // chunks held per lane (56 registers)
+constexpr int kMaxPersistLaunches = 16;
+
+struct PersistShape {
+    int C;            // 64-piece chunks per token row
+    int t0;           // first token of this launch
+    int64_t chunks;   // chunks of this launch: (its tokens) * C
+    int Q;            // chunks per wave, <= kHold
+};
+
+// One 16-byte output piece v of token t: the fixed-order FMA chain over the
+// token's entries, rounded to bf16.  An entry without a slot loads receive
+// row 0 (which always exists) and its FMA result is discarded by a select,
+// so that the slot loads do not depend on each other.  EXACT: k == KB, a
+// compile-time count, so that the token's slots and weights are unconditional
+// (merged) scalar loads.
+template <int KB, bool EXACT>
+__device__ __forceinline__ u32x4 combine_piece(const u32x4* __restrict__ eo, int nvec, int k_arg,
+                                               const int32_t* __restrict__ slots,
+                                               const float* __restrict__ w, int64_t R, int v) {
+    const int k = EXACT ? KB : k_arg;
+    float acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+    for (int j0 = 0; j0 < k; j0 += KB) {
+        bool ok[KB];
+        float wj[KB];
+        u32x4 buf[KB];
+#pragma unroll
+        for (int jj = 0; jj < KB; ++jj) {
+            const int j = j0 + jj;
+            const int32_t s = (j < k) ? slots[j] : -1;
+            ok[jj] = s >= 0 && s < R;
+            wj[jj] = (j < k) ? w[j] : 0.0f;
+            buf[jj] = __builtin_nontemporal_load(eo + static_cast<int64_t>(ok[jj] ? s : 0) * nvec + v);
+        }
+        // all of the batch's loads are issued before the first is used
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int jj = 0; jj < KB; ++jj) {
+            const u32x4 p = buf[jj];
+            const float f[8] = {lo16(p.x), hi16(p.x), lo16(p.y), hi16(p.y),
+                                lo16(p.z), hi16(p.z), lo16(p.w), hi16(p.w)};
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const float a = __builtin_fmaf(wj[jj], f[c], acc[c]);
+                acc[c] = ok[jj] ? a : acc[c];
+            }
+        }
+    }
+    u32x4 r;
+    r.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+    r.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+    r.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
+    r.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+    return r;
+}
+
+// One workgroup per CU is four waves per SIMD; telling the compiler so lets
+// it keep all of a chunk's row loads in flight instead of trading them for
+// registers.
+template <int KB, bool EXACT>
+__global__ __launch_bounds__(kPersistThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void combine_persistent_kernel(
+        const u32x4* __restrict__ eo, int nvec, int k, const int32_t* __restrict__ slot_of,
+        int64_t R, const float* __restrict__ weights, u32x4* __restrict__ y, PersistShape ps) {
+    const int lane = static_cast<int>(lane_id());
+    // the same for every lane of a wave: scalar from here on
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int64_t gw = static_cast<int64_t>(blockIdx.x) * kPersistWaves + wave;
+    const int64_t wbegin = gw * ps.Q;
+    const int64_t wend = min(wbegin + ps.Q, ps.chunks);
+    if (wbegin >= wend) return;  // uniform across the wave
+    const int n = static_cast<int>(wend - wbegin);
+    int t = static_cast<int>(wbegin / ps.C);
+    int cc = static_cast<int>(wbegin - static_cast<int64_t>(t) * ps.C);
+    t += ps.t0;
+    const int t_first = t, cc_first = cc;
+    u32x4 out[kHold];
+    uint32_t dep = 0;
+#pragma unroll
+    for (int i = 0; i < kHold; ++i) {
+        if (i < n) {  // uniform
+            int v = min(cc * kWave + lane, nvec - 1);
+            // this chunk's loads may not move above the previous result
+            asm volatile("" : "+v"(v) : "v"(dep));
+            out[i] = combine_piece<KB, EXACT>(eo, nvec, k, slot_of + static_cast<int64_t>(t) * k,
+                                              weights + static_cast<int64_t>(t) * k, R, v);
+            dep = out[i].x;
+            if (++cc == ps.C) {
+                cc = 0;
+                ++t;
+            }
+        }
+    }
+    t = t_first;
+    cc = cc_first;
+#pragma unroll
+    for (int i = 0; i < kHold; ++i) {
+        if (i < n) {
+            const int v = min(cc * kWave + lane, nvec - 1);
+            __builtin_nontemporal_store(out[i], y + static_cast<int64_t>(t) * nvec + v);
+            if (++cc == ps.C) {
+                cc = 0;
+                ++t;
+            }
+        }
+    }
+}
+
 template <int KB>
 void launch_kb(dim3 grid, int threads, hipStream_t stream, const u32x4* eo, int nvec, int k,
                const int32_t* slot_of, int64_t R, const float* w, u32x4* y) {
     hipLaunchKernelGGL((combine_kernel<KB, 2>), grid, dim3(threads), 0, stream, eo, nvec, k,
                        slot_of, R, w, y);
+}
+
+// k <= 8: KB = k exactly; larger k: batches of 8.
+template <int KB>
+void launch_persistent(int nwg, hipStream_t stream, const u32x4* eo, int nvec, int k,
+                       const int32_t* slot_of, int64_t R, const float* w, u32x4* y,
+                       const PersistShape& ps) {
+    if (k == KB)
+        hipLaunchKernelGGL((combine_persistent_kernel<KB, true>), dim3(nwg),
+                           dim3(kPersistThreads), 0, stream, eo, nvec, k, slot_of, R, w, y, ps);
+    else
+        hipLaunchKernelGGL((combine_persistent_kernel<KB, false>), dim3(nwg),
+                           dim3(kPersistThreads), 0, stream, eo, nvec, k, slot_of, R, w, y, ps);
 }
 
 }  // namespace
@@ -128,11 +272,57 @@ hipError_t launch_combine(const ep_problem& p, const void* expert_out, const int
     const int64_t R = p.capacity == 0 ? static_cast<int64_t>(T) * p.num_topk
                                       : static_cast<int64_t>(p.num_experts) * p.capacity;
     const int nvec = p.hidden / 8;
-    const TileShape s = row_tile_shape(nvec, 2);
-    const dim3 grid(T, s.tiles);
     const auto* eo = static_cast<const u32x4*>(expert_out);
     auto* yo = static_cast<u32x4*>(y);
     const int k = p.num_topk;
+
+    // Persistent form when every wave of one workgroup per CU gets at least
+    // one chunk: launches over consecutive token ranges of at most kHold
+    // chunks per wave each, up to kMaxPersistLaunches of them (more would
+    // pay more in launch gaps than the aligned phases save).
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return hipGetLastError();
+    const int C = (nvec + kWave - 1) / kWave;
+    const int64_t nw = static_cast<int64_t>(ncu) * kPersistWaves;
+    const int64_t all_chunks = static_cast<int64_t>(T) * C;
+    int64_t launches = (all_chunks + nw * kHold - 1) / (nw * kHold);
+    int64_t per = 0;  // tokens per launch, so that no wave gets more than kHold chunks
+    for (;; ++launches) {
+        per = (T + launches - 1) / launches;
+        if ((per * C + nw - 1) / nw <= kHold) break;
+    }
+    // The waves run nearly in step, reading the same column chunk of their
+    // rows at the same time; for rows that are a multiple of 4 KiB those are
+    // the same address bits below the row and pile onto the same HBM
+    // channels, and the per-token kernel is as fast or faster there
+    // (measured at H = 4096; at H = 7168 the persistent form won at every
+    // batch size tried, 2048 to 16384 tokens).
+    const bool spread = (static_cast<int64_t>(nvec) * 16) % 4096 != 0;
+    if (spread && all_chunks >= nw && launches <= kMaxPersistLaunches) {
+        for (int64_t t0 = 0; t0 < T; t0 += per) {
+            PersistShape ps;
+            ps.C = C;
+            ps.t0 = static_cast<int>(t0);
+            ps.chunks = min(per, static_cast<int64_t>(T) - t0) * C;
+            ps.Q = static_cast<int>((ps.chunks + nw - 1) / nw);
+            switch (k) {
+                case 1: launch_persistent<1>(ncu, stream, eo, nvec, k, slot_of, R, topk_weights, yo, ps); break;
+                case 2: launch_persistent<2>(ncu, stream, eo, nvec, k, slot_of, R, topk_weights, yo, ps); break;
+                case 3: launch_persistent<3>(ncu, stream, eo, nvec, k, slot_of, R, topk_weights, yo, ps); break;
+                case 4: launch_persistent<4>(ncu, stream, eo, nvec, k, slot_of, R, topk_weights, yo, ps); break;
+                case 5: launch_persistent<5>(ncu, stream, eo, nvec, k, slot_of, R, topk_weights, yo, ps); break;
+                case 6: launch_persistent<6>(ncu, stream, eo, nvec, k, slot_of, R, topk_weights, yo, ps); break;
+                case 7: launch_persistent<7>(ncu, stream, eo, nvec, k, slot_of, R, topk_weights, yo, ps); break;
+                default: launch_persistent<8>(ncu, stream, eo, nvec, k, slot_of, R, topk_weights, yo, ps); break;
+            }
+        }
+        return hipGetLastError();
+    }
+
+    const TileShape s = row_tile_shape(nvec, 2);
+    const dim3 grid(T, s.tiles);
     switch (k) {
         case 1: launch_kb<1>(grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
         case 2: launch_kb<2>(grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;

@@ -217,6 +217,10 @@ EDGE = [
     dict(T=2300, H=256, k=6, E=20, cap=700, fp8=False, name="ranked_capacity_overflow_bf16_k6"),
     # FP8 with k < 8 above 8192 entries: the layout kernels, then dispatch
     dict(T=2300, H=512, k=6, E=20, cap=700, fp8=True, name="fp8_k6_capacity_overflow"),
+    # the persistent combine (rows not a multiple of 4 KiB, at least one
+    # 64-piece chunk per wave of one workgroup per CU) with k > 8: entries in
+    # batches of 8
+    dict(T=2200, H=1536, k=16, E=64, cap=0, fp8=False, name="persistent_combine_k16"),
 ]
 
 
@@ -248,7 +252,9 @@ def test_duplicate_and_invalid_ids():
 
 def test_duplicate_and_invalid_ids_large_table():
     """The same id mix above 8192 entries (two-kernel layout; ranking inside
-    the dispatch kernel of ep_layout_dispatch), with and without capacity."""
+    the dispatch kernel of ep_layout_dispatch), with and without capacity, at
+    a size the persistent combine takes (tokens with no valid entry
+    included)."""
     rng = np.random.default_rng(10)
     T, k, E = 2100, 8, 40
     ids = rng.integers(0, E, size=(T, k))
@@ -257,9 +263,10 @@ def test_duplicate_and_invalid_ids_large_table():
     ids[::13, 3] = E
     ids[::17, 0] = 1 << 30
     ids[100:140] = 5                               # a run of one expert across tokens
+    ids[200:203] = -1                              # tokens without any valid entry
     for cap, fp8, fused in ((0, False, False), (0, False, True), (300, True, False),
                             (300, True, True), (0, 2, True)):
-        c = _random_case(T, 256, k, E, cap, fp8, seed=cap + 1, ids=ids,
+        c = _random_case(T, 640, k, E, cap, fp8, seed=cap + 1, ids=ids,
                          name=f"dup_invalid_large_cap{cap}_fp8{int(fp8)}")
         got = run_gpu(c, fused=fused)
         check_case(c, got)
