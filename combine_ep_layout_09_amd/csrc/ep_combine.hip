@@ -281,9 +281,10 @@ hipError_t launch_combine(const ep_problem& p, const void* expert_out, const int
     // chunks per wave each, up to kMaxPersistLaunches of them (more would
     // pay more in launch gaps than the aligned phases save).
     int dev = 0, ncu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return hipGetLastError();
+    hipError_t err = hipGetDevice(&dev);
+    if (err == hipSuccess)
+        err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess) return err;
     const int C = (nvec + kWave - 1) / kWave;
     const int64_t nw = static_cast<int64_t>(ncu) * kPersistWaves;
     const int64_t all_chunks = static_cast<int64_t>(T) * C;
@@ -317,8 +318,10 @@ hipError_t launch_combine(const ep_problem& p, const void* expert_out, const int
                 case 7: launch_persistent<7>(ncu, stream, eo, nvec, k, slot_of, R, topk_weights, yo, ps); break;
                 default: launch_persistent<8>(ncu, stream, eo, nvec, k, slot_of, R, topk_weights, yo, ps); break;
             }
+            err = hipGetLastError();
+            if (err != hipSuccess) return err;
         }
-        return hipGetLastError();
+        return hipSuccess;
     }
 
     const TileShape s = row_tile_shape(nvec, 2);

@@ -221,6 +221,9 @@ EDGE = [
     # 64-piece chunk per wave of one workgroup per CU) with k > 8: entries in
     # batches of 8
     dict(T=2200, H=1536, k=16, E=64, cap=0, fp8=False, name="persistent_combine_k16"),
+    # two launches of unequal token ranges (7501 + 7500 tokens), ragged
+    # chunks (225 pieces per row: 3 full chunks and one of 33)
+    dict(T=15001, H=1800, k=2, E=16, cap=0, fp8=False, name="persistent_combine_two_launches"),
 ]
 
 
