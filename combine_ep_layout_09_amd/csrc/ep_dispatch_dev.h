@@ -54,13 +54,20 @@ struct Bf16Tile {
     }
 };
 
-// Maximum across the 16 lanes of a DPP row (all lanes get the result).
+// Maximum across the 16 lanes of a DPP row (all lanes get the result), for
+// values >= 0: rotating the row right by 8, 4, 2 and 1 lanes and keeping the
+// larger value leaves every lane with the maximum of all 16.  Non-negative
+// floats order like their bit patterns, so the comparison is on integers,
+// and the lane moves are DPP operands rather than LDS round trips.
+constexpr int kDppRowRor = 0x120;  // row_ror:n is kDppRowRor + n
+
 __device__ __forceinline__ float row16_max(float m) {
-    m = fmaxf(m, __shfl_xor(m, 1, 16));
-    m = fmaxf(m, __shfl_xor(m, 2, 16));
-    m = fmaxf(m, __shfl_xor(m, 4, 16));
-    m = fmaxf(m, __shfl_xor(m, 8, 16));
-    return m;
+    uint32_t b = __float_as_uint(m);
+    b = max(b, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b), kDppRowRor + 8, 0xf, 0xf, false)));
+    b = max(b, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b), kDppRowRor + 4, 0xf, 0xf, false)));
+    b = max(b, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b), kDppRowRor + 2, 0xf, 0xf, false)));
+    b = max(b, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(b), kDppRowRor + 1, 0xf, 0xf, false)));
+    return __uint_as_float(b);
 }
 
 // E4M3 codes of the 8 channels of one 16-byte piece, each the code of the
