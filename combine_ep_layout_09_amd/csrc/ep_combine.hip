@@ -244,10 +244,14 @@ void combine_persistent_kernel(
 }
 
 template <int KB>
-void launch_kb(dim3 grid, int threads, hipStream_t stream, const u32x4* eo, int nvec, int k,
-               const int32_t* slot_of, int64_t R, const float* w, u32x4* y) {
-    hipLaunchKernelGGL((combine_kernel<KB, 2>), grid, dim3(threads), 0, stream, eo, nvec, k,
-                       slot_of, R, w, y);
+void launch_kb(int vpl, dim3 grid, int threads, hipStream_t stream, const u32x4* eo, int nvec,
+               int k, const int32_t* slot_of, int64_t R, const float* w, u32x4* y) {
+    if (vpl == 1)
+        hipLaunchKernelGGL((combine_kernel<KB, 1>), grid, dim3(threads), 0, stream, eo, nvec, k,
+                           slot_of, R, w, y);
+    else
+        hipLaunchKernelGGL((combine_kernel<KB, 2>), grid, dim3(threads), 0, stream, eo, nvec, k,
+                           slot_of, R, w, y);
 }
 
 // k <= 8: KB = k exactly; larger k: batches of 8.
@@ -324,17 +328,28 @@ hipError_t launch_combine(const ep_problem& p, const void* expert_out, const int
         return hipSuccess;
     }
 
-    const TileShape s = row_tile_shape(nvec, 2);
+    TileShape s = row_tile_shape(nvec, 2);
+    int vpl = 2;
+    if (static_cast<int64_t>(T) * s.tiles < 2 * static_cast<int64_t>(ncu)) {
+        // Small batches (decode): one piece per lane and narrower column
+        // tiles, so that every CU gets about two workgroups.
+        const int want = static_cast<int>(min(static_cast<int64_t>((nvec + 63) / 64),
+                                              (2 * static_cast<int64_t>(ncu) + T - 1) / T));
+        const int per = (nvec + want - 1) / want;
+        s.threads = min(1024, ((per + 63) / 64) * 64);
+        s.tiles = (nvec + s.threads - 1) / s.threads;
+        vpl = 1;
+    }
     const dim3 grid(T, s.tiles);
     switch (k) {
-        case 1: launch_kb<1>(grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
-        case 2: launch_kb<2>(grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
-        case 3: launch_kb<3>(grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
-        case 4: launch_kb<4>(grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
-        case 5: launch_kb<5>(grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
-        case 6: launch_kb<6>(grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
-        case 7: launch_kb<7>(grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
-        default: launch_kb<8>(grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
+        case 1: launch_kb<1>(vpl, grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
+        case 2: launch_kb<2>(vpl, grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
+        case 3: launch_kb<3>(vpl, grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
+        case 4: launch_kb<4>(vpl, grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
+        case 5: launch_kb<5>(vpl, grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
+        case 6: launch_kb<6>(vpl, grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
+        case 7: launch_kb<7>(vpl, grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
+        default: launch_kb<8>(vpl, grid, s.threads, stream, eo, nvec, k, slot_of, R, topk_weights, yo); break;
     }
     return hipGetLastError();
 }
