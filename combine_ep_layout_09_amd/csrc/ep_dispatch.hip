@@ -93,9 +93,16 @@ TileShape row_tile_shape(int nvec, int vpl) {
 // as many lanes as the row needs (up to 1024).  The pieces of a lane are all
 // loaded before the first store.
 DispatchShape dispatch_shape(int nvec, int T, bool fp8) {
-    // Few tokens (decode batches): wide workgroups, one piece per lane, so
-    // that enough waves exist to keep HBM busy.
-    if (T < 1024) return {1, row_tile_shape(nvec, 1)};
+    // Few tokens (decode batches): one piece per lane, and the row split into
+    // as many column tiles as it takes to have about 512 workgroups (two per
+    // CU), each at least one wave wide, so that enough waves exist to keep
+    // HBM busy.
+    if (T < 1024) {
+        const int want = min((nvec + 63) / 64, (512 + T - 1) / T);
+        const int per = (nvec + want - 1) / want;
+        const int threads = min(1024, ((per + 63) / 64) * 64);
+        return {1, {threads, (nvec + threads - 1) / threads}};
+    }
     if (nvec <= 128) return {1, {((nvec + 63) / 64) * 64, 1}};
     // FP8: quantising holds each piece's raw and encoded forms at once, so two
     // pieces per lane keep the kernel at full occupancy (eight waves per SIMD).
