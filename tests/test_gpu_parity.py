@@ -236,6 +236,49 @@ def test_edge_shapes(spec, fused):
     check_case(c, run_gpu(c, fused=fused))
 
 
+def _random_shapes(n, seed=2026):
+    """Seeded random problem shapes across every launch rule of the library:
+    one-launch and two-launch layout+dispatch, FP8 with small and large k,
+    capacity with and without overflow, decode-sized and prefill-sized
+    combines (persistent and per-token, ragged rows), all three payload
+    modes.  Even entries are decode-sized, odd ones prefill-sized (more than
+    8192 routing entries); receive buffers stay under about 150 MB."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        large = len(out) % 2 == 1
+        fp8 = int(rng.integers(0, 3))
+        if large:
+            T = int(rng.integers(1100, 20000))
+            k = int(rng.choice([5, 6, 8, 8, 9, 16]))
+        else:
+            T = int(np.exp(rng.uniform(0, np.log(1000))))
+            k = int(rng.choice([1, 2, 3, 5, 6, 8, 8, 16]))
+        E = int(rng.choice([1, 3, 16, 64, 100, 256, 1000]))
+        cap = 0 if rng.random() < 0.6 else int(rng.integers(1, max(2, 2 * T * k // E + 2)))
+        R = T * k if cap == 0 else E * cap
+        unit = 128 if fp8 else 8
+        hmax = int(min(6144, 150e6 / (2 * R))) // unit * unit
+        if hmax < unit or (large and T * k <= 8192):
+            continue
+        H = int(rng.integers(1, hmax // unit + 1)) * unit
+        out.append(dict(T=T, H=H, k=k, E=E, cap=cap, fp8=fp8,
+                        name=f"r{len(out)}_T{T}_H{H}_k{k}_E{E}_c{cap}_m{fp8}"))
+    return out
+
+
+RANDOM_SHAPES = _random_shapes(24)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+@pytest.mark.parametrize("spec", RANDOM_SHAPES, ids=[e["name"] for e in RANDOM_SHAPES])
+def test_random_shapes(spec, fused):
+    spec = dict(spec)
+    name = spec.pop("name")
+    c = _random_case(**spec, seed=zlib.crc32(name.encode()) % 1000, name=name)
+    check_case(c, run_gpu(c, fused=fused))
+
+
 def test_duplicate_and_invalid_ids():
     rng = np.random.default_rng(9)
     T, k, E = 700, 4, 12
