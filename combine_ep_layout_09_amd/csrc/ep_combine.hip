@@ -11,8 +11,12 @@
 // holds).  Every lane follows exactly that chain for each of its channels, so
 // the result does not depend on the launch shape.
 //
-// Launch shape: one workgroup per (token, column tile), VPL 16-byte pieces
-// per lane spaced one workgroup-width apart (the same tiling as dispatch).
+// Two launch forms compute exactly this chain.  Prefill-sized batches whose
+// rows are not a multiple of 4 KiB use the persistent form further down
+// (every wave reads all its rows before it writes).  Otherwise: one
+// workgroup per (token, column tile), VPL 16-byte pieces per lane spaced one
+// workgroup-width apart (the same tiling as dispatch; small batches take one
+// piece per lane and narrower tiles, so that every CU gets work).
 // Entries are taken in batches of KB: the lane first issues the loads of all
 // KB expert rows for all its pieces -- with no branches, so they are all in
 // flight together -- and then runs the FMA chain.  An entry without a slot
