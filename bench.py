@@ -200,9 +200,9 @@ def fused_call_name(wl):
 
 def combine_kernel_name(wl, ncu):
     """The kernel ep_combine runs on this workload (the library's rule: the
-    persistent form when rows are not a multiple of 4 KiB, every wave of one
-    1024-lane workgroup per CU gets at least one 64-piece chunk, and at most
-    16 launches of at most 14 chunks per wave cover the batch)."""
+    persistent form when every wave of one 1024-lane workgroup per CU gets at
+    least one 64-piece chunk and at most 16 launches of at most 14 chunks per
+    wave cover the batch)."""
     nvec = wl.H // 8
     C = -(-nvec // 64)
     nw = ncu * 16
@@ -210,7 +210,7 @@ def combine_kernel_name(wl, ncu):
     launches = max(1, -(-chunks // (nw * 14)))
     while -(-(-(-wl.T // launches) * C) // nw) > 14:
         launches += 1
-    if (nvec * 16) % 4096 != 0 and chunks >= nw and launches <= 16:
+    if chunks >= nw and launches <= 16:
         return "combine_persistent_kernel"
     return "combine_kernel"
 

@@ -11,9 +11,9 @@
 // holds).  Every lane follows exactly that chain for each of its channels, so
 // the result does not depend on the launch shape.
 //
-// Two launch forms compute exactly this chain.  Prefill-sized batches whose
-// rows are not a multiple of 4 KiB use the persistent form further down
-// (every wave reads all its rows before it writes).  Otherwise: one
+// Two launch forms compute exactly this chain.  Prefill-sized batches use
+// the persistent form further down (every wave reads all its rows before it
+// writes).  Otherwise: one
 // workgroup per (token, column tile), VPL 16-byte pieces per lane spaced one
 // workgroup-width apart (the same tiling as dispatch; small batches take one
 // piece per lane and narrower tiles, so that every CU gets work).
@@ -123,10 +123,10 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(
 // runs well below the rate of the loads alone (measured: the prefill
 // combine's loads alone take about 70 us, its stores alone about 13 us,
 // interleaved about 93 us).  Here one 1024-lane workgroup per CU owns a
-// contiguous run of (token, 64-piece chunk) units per wave, computes up to
-// kHold of them into registers -- one chunk at a time per wave, since its
-// loads must not be hoisted into the held registers -- and only then stores
-// them.  Every wave does the same amount of work from the same start, so
+// contiguous run of (token, 64-piece chunk) units, each of its waves up to
+// kHold of them, which it computes into registers -- one chunk at a time per
+// wave, since its loads must not be hoisted into the held registers -- and
+// only then stores.  Every wave does the same amount of work from the same start, so
 // the waves of the whole chip reach their store bursts at about the same
 // time, without any barrier.  Larger problems take one launch per kHold
 // chunks per wave, over consecutive token ranges: a kernel boundary keeps
@@ -141,10 +141,10 @@ constexpr int kHold = 14;  // chunks held per lane (56 registers)
 constexpr int kMaxPersistLaunches = 16;
 
 struct PersistShape {
-    int C;            // 64-piece chunks per token row
-    int t0;           // first token of this launch
-    int64_t chunks;   // chunks of this launch: (its tokens) * C
-    int Q;            // chunks per wave, <= kHold
+    int C;        // 64-piece chunks per token row
+    int t0;       // first token of this launch
+    int chunks;   // chunks of this launch: (its tokens) * C, <= waves * kHold
+    int Q;        // chunks per wave, <= kHold
 };
 
 // One 16-byte output piece v of token t: the fixed-order FMA chain over the
@@ -206,43 +206,41 @@ void combine_persistent_kernel(
     const int lane = static_cast<int>(lane_id());
     // the same for every lane of a wave: scalar from here on
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
-    const int64_t gw = static_cast<int64_t>(blockIdx.x) * kPersistWaves + wave;
-    const int64_t wbegin = gw * ps.Q;
-    const int64_t wend = min(wbegin + ps.Q, ps.chunks);
-    if (wbegin >= wend) return;  // uniform across the wave
-    const int n = static_cast<int>(wend - wbegin);
-    int t = static_cast<int>(wbegin / ps.C);
-    int cc = static_cast<int>(wbegin - static_cast<int64_t>(t) * ps.C);
-    t += ps.t0;
-    const int t_first = t, cc_first = cc;
+    // Workgroup b owns the contiguous chunks [b * 16 Q, (b + 1) * 16 Q) of the
+    // launch; wave w takes chunks w, w + 16, w + 32, ... of them, so that the
+    // waves of a CU work on neighbouring chunks -- different column chunks of
+    // a few rows -- at any time.  With a contiguous run per wave, all waves
+    // of the chip read the same column chunk of their rows at once, which for
+    // rows of a multiple of 4 KiB lands on the same HBM channels (measured
+    // at H = 4096: 57.8 us against 52.9 us for the per-token kernel; strided,
+    // 52.4 us).
+    const int base = static_cast<int>(blockIdx.x) * kPersistWaves * ps.Q + wave;
+    auto chunk_of = [&](int i, int& t, int& v) {
+        const int c = base + i * kPersistWaves;  // chunks of one launch < 2^31
+        const int tt = c / ps.C;
+        t = ps.t0 + tt;
+        v = min((c - tt * ps.C) * kWave + lane, nvec - 1);
+    };
     u32x4 out[kHold];
     uint32_t dep = 0;
 #pragma unroll
     for (int i = 0; i < kHold; ++i) {
-        if (i < n) {  // uniform
-            int v = min(cc * kWave + lane, nvec - 1);
+        if (i < ps.Q && base + i * kPersistWaves < ps.chunks) {  // uniform
+            int t, v;
+            chunk_of(i, t, v);
             // this chunk's loads may not move above the previous result
             asm volatile("" : "+v"(v) : "v"(dep));
             out[i] = combine_piece<KB, EXACT>(eo, nvec, k, slot_of + static_cast<int64_t>(t) * k,
                                               weights + static_cast<int64_t>(t) * k, R, v);
             dep = out[i].x;
-            if (++cc == ps.C) {
-                cc = 0;
-                ++t;
-            }
         }
     }
-    t = t_first;
-    cc = cc_first;
 #pragma unroll
     for (int i = 0; i < kHold; ++i) {
-        if (i < n) {
-            const int v = min(cc * kWave + lane, nvec - 1);
+        if (i < ps.Q && base + i * kPersistWaves < ps.chunks) {
+            int t, v;
+            chunk_of(i, t, v);
             __builtin_nontemporal_store(out[i], y + static_cast<int64_t>(t) * nvec + v);
-            if (++cc == ps.C) {
-                cc = 0;
-                ++t;
-            }
         }
     }
 }
@@ -302,19 +300,12 @@ hipError_t launch_combine(const ep_problem& p, const void* expert_out, const int
         per = (T + launches - 1) / launches;
         if ((per * C + nw - 1) / nw <= kHold) break;
     }
-    // The waves run nearly in step, reading the same column chunk of their
-    // rows at the same time; for rows that are a multiple of 4 KiB those are
-    // the same address bits below the row and pile onto the same HBM
-    // channels, and the per-token kernel is as fast or faster there
-    // (measured at H = 4096; at H = 7168 the persistent form won at every
-    // batch size tried, 2048 to 16384 tokens).
-    const bool spread = (static_cast<int64_t>(nvec) * 16) % 4096 != 0;
-    if (spread && all_chunks >= nw && launches <= kMaxPersistLaunches) {
+    if (all_chunks >= nw && launches <= kMaxPersistLaunches) {
         for (int64_t t0 = 0; t0 < T; t0 += per) {
             PersistShape ps;
             ps.C = C;
             ps.t0 = static_cast<int>(t0);
-            ps.chunks = min(per, static_cast<int64_t>(T) - t0) * C;
+            ps.chunks = static_cast<int>(min(per, static_cast<int64_t>(T) - t0) * C);
             ps.Q = static_cast<int>((ps.chunks + nw - 1) / nw);
             switch (k) {
                 case 1: launch_persistent<1>(ncu, stream, eo, nvec, k, slot_of, R, topk_weights, yo, ps); break;

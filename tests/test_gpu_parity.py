@@ -217,9 +217,8 @@ EDGE = [
     dict(T=2300, H=256, k=6, E=20, cap=700, fp8=False, name="ranked_capacity_overflow_bf16_k6"),
     # FP8 with k < 8 above 8192 entries: the layout kernels, then dispatch
     dict(T=2300, H=512, k=6, E=20, cap=700, fp8=True, name="fp8_k6_capacity_overflow"),
-    # the persistent combine (rows not a multiple of 4 KiB, at least one
-    # 64-piece chunk per wave of one workgroup per CU) with k > 8: entries in
-    # batches of 8
+    # the persistent combine (at least one 64-piece chunk per wave of one
+    # workgroup per CU) with k > 8: entries in batches of 8
     dict(T=2200, H=1536, k=16, E=64, cap=0, fp8=False, name="persistent_combine_k16"),
     # two launches of unequal token ranges (7501 + 7500 tokens), ragged
     # chunks (225 pieces per row: 3 full chunks and one of 33)
