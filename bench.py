@@ -182,17 +182,43 @@ def one_launch(wl):
     return n <= 8192 and n * nwg <= (1 << 23)
 
 
+def persistent_launch(wl, ncu):
+    """Whether ep_layout_dispatch takes its one-launch form of one 1024-lane
+    workgroup per CU (the library's rule: bf16 rows, 8192 < T*k <= 32768,
+    T*k a multiple of 4, between 1 and 14 chunks of 64 pieces per wave, the
+    workgroup's own entries within 1024 and its LDS within 64 KiB)."""
+    n = wl.T * wl.k
+    if wl.fp8 or n <= 8192 or n > 32768 or n % 4:
+        return False
+    C = -(-(wl.H // 8) // 64)
+    nw = ncu * 16
+    chunks = wl.T * C
+    if chunks < nw or chunks > nw * 14:
+        return False
+    Q = -(-chunks // nw)
+    maxtok = (16 * Q - 1) // C + 2
+    own = maxtok * wl.k
+    if own > 1024:
+        return False
+    rw = -(-own // 64)
+    head = ((3 + rw) * (wl.E + 1) + 3) & ~3
+    return (head + maxtok * ((wl.k + 3) & ~3)) * 4 <= 65536
+
+
 # sources of every kernel an ep_layout_dispatch call may launch
-FUSED_SOURCES = ("ep_fused.hip", "ep_layout.hip", "ep_dispatch.hip")
+FUSED_SOURCES = ("ep_fused.hip", "ep_fused_persist.hip", "ep_layout.hip", "ep_dispatch.hip")
 
 
-def fused_call_name(wl):
+def fused_call_name(wl, ncu):
     """The kernels of one ep_layout_dispatch call on this workload (the
-    library's rule: one kernel for small tables; the histogram kernel and the
-    ranking dispatch kernel for bf16 rows or k >= 8; otherwise the layout
-    kernels and the dispatch kernel)."""
+    library's rule: one kernel for small tables; one persistent kernel for
+    prefill-sized bf16 tables that fit it; the histogram kernel and the
+    ranking dispatch kernel for other bf16 rows or k >= 8; otherwise the
+    layout kernels and the dispatch kernel)."""
     if one_launch(wl):
         return "layout_dispatch_small_kernel"
+    if persistent_launch(wl, ncu):
+        return "layout_dispatch_persistent_kernel"
     if not wl.fp8 or wl.k >= 8:
         return "layout_hist_kernel+layout_dispatch_ranked_kernel"
     return "layout_hist_kernel+layout_rank_kernel+dispatch_fp8_kernel"
@@ -380,15 +406,16 @@ def main():
     total_bytes = nb["dispatch_total"] + nb["combine_total"]
     value = total_bytes / (ms_per_step / 1e3) / 1e9
 
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
     if fused:
         # the whole ep_layout_dispatch call: the layout's and the dispatch's
         # algorithmic bytes, over the call's duration
-        disp_entry = (fused_call_name(wl),
+        disp_entry = (fused_call_name(wl, ncu),
                       (dispatch_ms, nb["dispatch_total"], FUSED_SOURCES))
     else:
         disp_entry = ("dispatch_bf16_kernel" if not wl.fp8 else "dispatch_fp8_kernel",
                       (dispatch_ms, nb["dispatch_kernel"], ("ep_dispatch.hip",)))
-    comb = combine_kernel_name(wl, torch.cuda.get_device_properties(0).multi_processor_count)
+    comb = combine_kernel_name(wl, ncu)
     kernels = {disp_entry[0]: disp_entry[1],
                comb: (combine_ms, nb["combine_kernel"], ("ep_combine.hip",))}
     dom = max(kernels, key=lambda n: kernels[n][0])

@@ -517,6 +517,13 @@ hipError_t launch_layout_dispatch(const ep_problem& p, const int32_t* topk_idx,
     // Every workgroup reads the whole table: past a few million id visits in
     // all, the layout kernels followed by the dispatch kernel are faster.
     if (n > kFusedMaxEntries || n * nwg > kFusedMaxVisits) {
+        int dev = 0, ncu = 0;
+        hipError_t err = hipGetDevice(&dev);
+        if (err == hipSuccess)
+            err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (err != hipSuccess) return err;
+        if (layout_dispatch_persistent_fits(p, ncu))
+            return launch_layout_dispatch_persistent(p, topk_idx, out, x, recv_x, ncu, stream);
         // Ranking inside the dispatch kernel puts two dependent round trips
         // (the token's ids, then its table columns) ahead of each
         // workgroup's row; that pays for bf16 rows and for FP8 with k >= 8,
@@ -525,7 +532,7 @@ hipError_t launch_layout_dispatch(const ep_problem& p, const int32_t* topk_idx,
         if (p.use_fp8 == 0 || p.num_topk >= 8)
             return launch_tables_ranked(p, topk_idx, out, static_cast<int32_t*>(workspace), x,
                                         recv_x, recv_scales, stream);
-        hipError_t err = launch_layout(p, topk_idx, out, static_cast<int32_t*>(workspace), stream);
+        err = launch_layout(p, topk_idx, out, static_cast<int32_t*>(workspace), stream);
         if (err != hipSuccess) return err;
         return launch_dispatch(p, x, out.slot_of, recv_x, recv_scales, stream);
     }

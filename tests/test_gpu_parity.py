@@ -206,17 +206,31 @@ EDGE = [
     # entries itself.  Tokens straddling layout blocks (k does not divide the
     # block size), more entries than 16-lane rows in a workgroup, blocks wider
     # than one pass over the ids, rows of two column tiles, few tokens with a
-    # wide k, one expert, capacity with overflow.
+    # wide k, one expert, capacity with overflow (shapes outside the
+    # one-launch form below: fewer than one chunk per wave, or T*k > 32768).
     dict(T=3000, H=256, k=5, E=50, cap=0, fp8=False, name="ranked_odd_k_straddle"),
-    dict(T=1024, H=2048, k=16, E=128, cap=0, fp8=False, name="ranked_k16_two_rounds"),
+    dict(T=1024, H=1024, k=16, E=128, cap=0, fp8=False, name="ranked_k16_two_rounds"),
     dict(T=4500, H=3584, k=8, E=96, cap=0, fp8=False, name="ranked_wide_blocks_bf16"),
-    dict(T=1100, H=9216, k=8, E=64, cap=0, fp8=False, name="ranked_two_tiles_bf16"),
+    dict(T=4100, H=9216, k=8, E=64, cap=0, fp8=False, name="ranked_two_tiles_bf16"),
     dict(T=600, H=1024, k=16, E=64, cap=0, fp8=True, name="ranked_few_tokens_k16"),
-    dict(T=9000, H=128, k=1, E=1, cap=0, fp8=False, name="ranked_one_expert"),
+    dict(T=40000, H=128, k=1, E=1, cap=0, fp8=False, name="ranked_one_expert"),
     dict(T=1800, H=512, k=8, E=20, cap=700, fp8=True, name="ranked_capacity_overflow"),
     dict(T=2300, H=256, k=6, E=20, cap=700, fp8=False, name="ranked_capacity_overflow_bf16_k6"),
     # FP8 with k < 8 above 8192 entries: the layout kernels, then dispatch
     dict(T=2300, H=512, k=6, E=20, cap=700, fp8=True, name="fp8_k6_capacity_overflow"),
+    # ep_layout_dispatch in one launch of one workgroup per CU (bf16 rows,
+    # 8192 < T*k <= 32768, at least one 64-piece chunk per wave): tokens
+    # straddling two workgroups and a partly filled last workgroup (5 chunks
+    # per row, 32 per workgroup), capacity with overflow, an odd k (slot rows
+    # padded to 4), k above 8 (the generic store loop), the most experts,
+    # the largest table with k = 32, one expert, ragged rows
+    dict(T=1500, H=2560, k=8, E=64, cap=0, fp8=False, name="persistent_dispatch_straddle"),
+    dict(T=2048, H=2048, k=8, E=64, cap=200, fp8=False, name="persistent_dispatch_capacity_overflow"),
+    dict(T=2400, H=1800, k=5, E=37, cap=0, fp8=False, name="persistent_dispatch_odd_k_ragged_row"),
+    dict(T=1300, H=3072, k=12, E=256, cap=0, fp8=False, name="persistent_dispatch_k12"),
+    dict(T=1700, H=2048, k=8, E=1024, cap=0, fp8=False, name="persistent_dispatch_max_experts"),
+    dict(T=1024, H=4096, k=32, E=128, cap=0, fp8=False, name="persistent_dispatch_k32_largest_table"),
+    dict(T=12000, H=512, k=2, E=1, cap=0, fp8=False, name="persistent_dispatch_one_expert"),
     # the persistent combine (at least one 64-piece chunk per wave of one
     # workgroup per CU) with k > 8: entries in batches of 8
     dict(T=2200, H=1536, k=16, E=64, cap=0, fp8=False, name="persistent_combine_k16"),
@@ -297,8 +311,9 @@ def test_duplicate_and_invalid_ids():
 
 def test_duplicate_and_invalid_ids_large_table():
     """The same id mix above 8192 entries (two-kernel layout; ranking inside
-    the dispatch kernel of ep_layout_dispatch), with and without capacity, at
-    a size the persistent combine takes (tokens with no valid entry
+    the dispatch kernel of ep_layout_dispatch at H = 256; one launch of one
+    workgroup per CU for bf16 rows at H = 640), with and without capacity,
+    at a size the persistent combine takes (tokens with no valid entry
     included)."""
     rng = np.random.default_rng(10)
     T, k, E = 2100, 8, 40
@@ -309,10 +324,12 @@ def test_duplicate_and_invalid_ids_large_table():
     ids[::17, 0] = 1 << 30
     ids[100:140] = 5                               # a run of one expert across tokens
     ids[200:203] = -1                              # tokens without any valid entry
-    for cap, fp8, fused in ((0, False, False), (0, False, True), (300, True, False),
-                            (300, True, True), (0, 2, True)):
-        c = _random_case(T, 640, k, E, cap, fp8, seed=cap + 1, ids=ids,
-                         name=f"dup_invalid_large_cap{cap}_fp8{int(fp8)}")
+    for H, cap, fp8, fused in ((640, 0, False, False), (640, 0, False, True),
+                               (640, 300, False, True), (256, 0, False, True),
+                               (640, 300, True, False), (640, 300, True, True),
+                               (640, 0, 2, True)):
+        c = _random_case(T, H, k, E, cap, fp8, seed=cap + 1, ids=ids,
+                         name=f"dup_invalid_large_H{H}_cap{cap}_fp8{int(fp8)}")
         got = run_gpu(c, fused=fused)
         check_case(c, got)
         assert got["status"][0] == int(((ids < 0) | (ids >= E)).sum())
