@@ -231,6 +231,11 @@ EDGE = [
     dict(T=1700, H=2048, k=8, E=1024, cap=0, fp8=False, name="persistent_dispatch_max_experts"),
     dict(T=1024, H=4096, k=32, E=128, cap=0, fp8=False, name="persistent_dispatch_k32_largest_table"),
     dict(T=12000, H=512, k=2, E=1, cap=0, fp8=False, name="persistent_dispatch_one_expert"),
+    # the persistent combine at 14 chunks per wave: a partly filled last
+    # workgroup with ragged rows (875 pieces per row: 13 full chunks and one
+    # of 43), and k = 1 with capacity drops (entries without a slot)
+    dict(T=4000, H=7000, k=5, E=64, cap=0, fp8=False, name="persistent_combine_ragged_partial"),
+    dict(T=4096, H=7168, k=1, E=16, cap=300, fp8=False, name="persistent_combine_k1_capacity"),
     # the persistent combine (at least one 64-piece chunk per wave of one
     # workgroup per CU) with k > 8: entries in batches of 8
     dict(T=2200, H=1536, k=16, E=64, cap=0, fp8=False, name="persistent_combine_k16"),
