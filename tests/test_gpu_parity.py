@@ -231,6 +231,12 @@ EDGE = [
     dict(T=1700, H=2048, k=8, E=1024, cap=0, fp8=False, name="persistent_dispatch_max_experts"),
     dict(T=1024, H=4096, k=32, E=128, cap=0, fp8=False, name="persistent_dispatch_k32_largest_table"),
     dict(T=12000, H=512, k=2, E=1, cap=0, fp8=False, name="persistent_dispatch_one_expert"),
+    # FP8 rows at prefill sizes (the multi-kernel forms): rows of 15 blocks
+    # (two 7-block tiles and a ragged one), UE8M0 scales with capacity
+    # overflow, 49152 entries over 48 experts
+    dict(T=2000, H=1920, k=8, E=64, cap=0, fp8=1, name="prefill_fp8_ragged_blocks"),
+    dict(T=3000, H=1024, k=6, E=32, cap=400, fp8=2, name="prefill_ue8m0_capacity_overflow"),
+    dict(T=8192, H=4096, k=6, E=48, cap=0, fp8=1, name="prefill_fp8_k6_48_experts"),
     # the persistent combine at 14 chunks per wave: a partly filled last
     # workgroup with ragged rows (875 pieces per row: 13 full chunks and one
     # of 43), and k = 1 with capacity drops (entries without a slot)
@@ -340,12 +346,8 @@ def test_duplicate_and_invalid_ids_large_table():
         assert got["status"][0] == int(((ids < 0) | (ids >= E)).sum())
 
 
-def test_fp8_special_rows():
-    """All-zero rows and blocks (scale 0), blocks of bf16 subnormals only,
-    negative zeros and tiny negatives, huge/tiny mixes whose quotients
-    underflow, x100 outliers, and quotients next to E4M3 rounding midpoints."""
-    rng = np.random.default_rng(31)
-    T, H, E, k = 12, 1024, 4, 2
+def _fp8_special_xf(rng, T, H):
+    """fp32 rows (T >= 6) whose first six rows hold the special FP8 cases."""
     xf = rng.standard_normal((T, H)).astype(np.float32)
     xf[0] = 0.0                                            # whole row zero
     xf[1, 128:256] = 0.0                                   # one zero block
@@ -363,7 +365,16 @@ def test_fp8_special_rows():
         xf[5, 128 * b: 128 * b + 126] = rng.choice(mids, 126) * 2.0 ** m * rng.choice([-1, 1], 126)
         xf[5, 128 * b + 126] = 448.0 * 2.0 ** m
         xf[5, 128 * b + 127] = -(2.0 ** (m - 10))            # exact tie with zero
-    x = workloads.to_bf16_bits(xf)
+    return xf
+
+
+def test_fp8_special_rows():
+    """All-zero rows and blocks (scale 0), blocks of bf16 subnormals only,
+    negative zeros and tiny negatives, huge/tiny mixes whose quotients
+    underflow, x100 outliers, and quotients next to E4M3 rounding midpoints."""
+    rng = np.random.default_rng(31)
+    T, H, E, k = 12, 1024, 4, 2
+    x = workloads.to_bf16_bits(_fp8_special_xf(rng, T, H))
     ids = np.stack([np.arange(T) % E, (np.arange(T) + 1) % E], axis=1).astype(np.int32)
     w = np.full((T, k), 0.5, np.float32)
     eo = workloads.to_bf16_bits(rng.standard_normal((T * k, H)).astype(np.float32))
@@ -421,6 +432,23 @@ def test_fp8_near_midpoint_quotients(fused):
     eo = workloads.to_bf16_bits(rng.standard_normal((T * k, H)).astype(np.float32))
     c = Case(T, H, k, E, 0, True, x, ids, w, eo, name="fp8_near_midpoint")
     check_case(c, run_gpu(c, fused=fused))
+
+
+@pytest.mark.parametrize("mode", [1, 2], ids=["fp32_scales", "ue8m0"])
+def test_fp8_special_rows_prefill_batch(mode):
+    """The special FP8 rows and near-midpoint rows inside a prefill-sized
+    batch (2048 tokens of 1024 channels, k = 5: above the small-table
+    forms)."""
+    rng = np.random.default_rng(41)
+    T, H, E, k = 2048, 1024, 16, 5
+    xf = _fp8_special_xf(rng, T, H)
+    x = workloads.to_bf16_bits(xf)
+    x[6:14] = _near_midpoint_rows(8, H, seed=79)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    eo = workloads.to_bf16_bits(rng.standard_normal((T * k, H)).astype(np.float32))
+    c = Case(T, H, k, E, 0, mode, x, ids, w, eo, name=f"fp8_special_prefill_m{mode}")
+    check_case(c, run_gpu(c, fused=True))
 
 
 @pytest.mark.parametrize("over", [dict(cid=3, T=1024, hot_experts=16, hot_ratio=3.0),
