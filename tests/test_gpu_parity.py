@@ -452,14 +452,19 @@ def test_fp8_special_rows_prefill_batch(mode):
 
 
 @pytest.mark.parametrize("over", [dict(cid=3, T=1024, hot_experts=16, hot_ratio=3.0),
+                                  dict(cid=3, T=2048, hot_experts=16, hot_ratio=3.0),
                                   dict(cid=4, T=2048, zipf_s=1.6),
                                   dict(cid=4, T=2048, zipf_s=0.8)],
-                         ids=["hot3x", "zipf1.6", "zipf0.8"])
+                         ids=["hot3x", "hot3x_one_launch", "zipf1.6", "zipf0.8"])
 def test_skew_sweep_variants(over):
-    """The routing-skew sweep's extreme variants, at reduced token counts."""
+    """The routing-skew sweep's extreme variants, at reduced token counts,
+    through the separate calls and ep_layout_dispatch (at 2048 prefill tokens
+    its one-launch form: hot experts put many LDS histogram atomics of a wave
+    on one address)."""
     over = dict(over)
     c = Case.from_workload(workloads.make(over.pop("cid"), **over))
     check_case(c, run_gpu(c))
+    check_case(c, run_gpu(c, fused=True))
 
 
 # ---------------------------------------------------------------------------
