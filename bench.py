@@ -205,8 +205,14 @@ def persistent_launch(wl, ncu):
     return (head + maxtok * ((wl.k + 3) & ~3)) * 4 <= 65536
 
 
-# sources of every kernel an ep_layout_dispatch call may launch
-FUSED_SOURCES = ("ep_fused.hip", "ep_fused_persist.hip", "ep_layout.hip", "ep_dispatch.hip")
+# sources of the kernels each form of an ep_layout_dispatch call launches (a
+# counter summary's digest covers these and the headers they include)
+FUSED_SOURCES = {
+    "layout_dispatch_small_kernel": ("ep_fused.hip",),
+    "layout_dispatch_persistent_kernel": ("ep_fused_persist.hip",),
+    "layout_hist_kernel+layout_dispatch_ranked_kernel": ("ep_fused.hip", "ep_layout.hip"),
+    "layout_hist_kernel+layout_rank_kernel+dispatch_fp8_kernel": ("ep_layout.hip", "ep_dispatch.hip"),
+}
 
 
 def fused_call_name(wl, ncu):
@@ -411,7 +417,7 @@ def main():
         # the whole ep_layout_dispatch call: the layout's and the dispatch's
         # algorithmic bytes, over the call's duration
         disp_entry = (fused_call_name(wl, ncu),
-                      (dispatch_ms, nb["dispatch_total"], FUSED_SOURCES))
+                      (dispatch_ms, nb["dispatch_total"], FUSED_SOURCES[fused_call_name(wl, ncu)]))
     else:
         disp_entry = ("dispatch_bf16_kernel" if not wl.fp8 else "dispatch_fp8_kernel",
                       (dispatch_ms, nb["dispatch_kernel"], ("ep_dispatch.hip",)))

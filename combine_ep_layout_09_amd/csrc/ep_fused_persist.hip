@@ -10,12 +10,11 @@
 // and every entry with a slot receives a bit copy of token t's row.
 //
 // Workgroup b owns a contiguous run of (token, 64-piece chunk) units -- 16 Q
-// of them, Q <= kHold per wave, dealt to its 16 waves in turn (wave w takes
-// chunks w, w + 16, ...) -- and so a contiguous run of tokens [tA, tB).
+// of them, Q <= kHold -- and so a contiguous run of tokens [tA, tB).
 // Nothing waits for another workgroup:
 //   1. every lane issues its first loads at once: the workgroup's own routing
 //      entries (one per lane), the whole routing table (kIdQuads quads per
-//      lane), then its first kLead rounds of row chunks;
+//      lane), then its wave's first kAhead row chunks;
 //   2. while the rows are in flight, the table builds two LDS histograms:
 //      the ids ahead of the workgroup's first entry, and the rest (the
 //      counting sort's "entries before i" split at the workgroup's start);
@@ -25,9 +24,10 @@
 //      an own entry's rank is the ids ahead of the workgroup with its
 //      expert, plus the own entries of earlier waves, plus the peers of
 //      lower lanes in its wave;
-//   4. every wave stores its chunks to the k receive rows of their tokens in
-//      rounds, loading the chunks of a later round while a round's stores
-//      drain.
+//   4. every wave stores chunks to the k receive rows of their tokens one
+//      step at a time, loading a later chunk while a step's stores drain;
+//      past its first kAhead chunks a wave takes the run's next chunk from
+//      an LDS counter, so that the waves of a workgroup finish together.
 // Every workgroup builds the same whole-table histogram (a read of the table
 // from L2 per CU): the price of needing no other workgroup, paid while the
 // workgroup's first rows arrive from HBM.  Workgroup 0 writes count, offset
@@ -54,11 +54,9 @@ using layout::wave_inclusive_scan;
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kHold = 14;        // row chunks held per lane (56 registers)
-constexpr int kRound = 2;        // chunks a wave stores per round
-constexpr int kLead = 2;         // rounds loaded ahead of the first store
-constexpr int kRounds = kHold / kRound;
-static_assert(kHold % kRound == 0 && kLead >= 1 && kLead <= kRounds, "whole rounds");
+constexpr int kHold = 14;        // row chunks per wave of one launch, at most (Q)
+constexpr int kAhead = 4;        // chunks a wave has loaded ahead of its next store
+constexpr int kRing = kAhead + 1;
 constexpr int kIdQuads = 8;      // routing-table quads per lane (32 ids)
 constexpr int kMaxIds = 4 * kIdQuads * kThreads;  // routing entries (T*k) of this form
 constexpr size_t kMaxLds = 65536;
@@ -140,23 +138,37 @@ void layout_dispatch_persistent_kernel(PersistParams p) {
     int4 q[kIdQuads];
 #pragma unroll
     for (int u = 0; u < kIdQuads; ++u) q[u] = quads[min(u * kThreads + tid, nq - 1)];
-    // ... and the first kLead rounds of row chunks.  Every load is issued, a
-    // chunk past the workgroup's run reading its last chunk again (a cache
-    // hit, never stored): with loads under branches the compiler could no
-    // longer count which of them are still in flight, and the histogram
-    // below would wait for the rows instead of only for the table.
-    const int cbase = c_begin + wave;
+    // ... and the wave's first kAhead row chunks (chunks w, w + 16, ... of
+    // the workgroup's run), into a ring of kRing slots; cid[s] is the chunk
+    // slot s holds, -1 for none.  Every load is issued -- a slot with no chunk
+    // reads the run's last chunk again (a cache hit, never stored) -- because
+    // with loads under branches the compiler could no longer count which of
+    // them are still in flight, and the histogram below would wait for the
+    // rows instead of only for the table.
     const int c_last = max(c_end - 1, 0);
-    u32x4 buf[kHold];
-    auto load_chunk = [&](int i) {
-        const int c = min(cbase + i * kWaves, c_last);
-        const int t = c / p.C;
-        const int v = min((c - t * p.C) * kWave + lane, p.nvec - 1);
-        buf[i] = p.x[static_cast<int64_t>(t) * p.nvec + v];
+    u32x4 buf[kRing];
+    int cid[kRing];
+    auto load_into = [&](int s, int c) {
+        const int cc = c >= 0 ? c : c_last;
+        const int t = cc / p.C;
+        const int v = min((cc - t * p.C) * kWave + lane, p.nvec - 1);
+        buf[s] = p.x[static_cast<int64_t>(t) * p.nvec + v];
+        cid[s] = c;
     };
 #pragma unroll
-    for (int i = 0; i < kLead * kRound; ++i) load_chunk(i);
+    for (int j = 0; j < kAhead; ++j) {
+        const int c = c_begin + wave + j * kWaves;
+        load_into(j, c < c_end ? c : -1);
+    }
+    cid[kAhead] = -1;
 
+    // Chunks past the first kAhead of every wave are handed out in turn by an
+    // LDS counter, to whichever wave comes for one next: a SIMD issues for
+    // its oldest wave first, and with a fixed share per wave the youngest
+    // waves finished up to twice as late as the oldest (measured), leaving
+    // the end of the kernel to a quarter of the waves.
+    __shared__ int s_next;
+    if (tid == 0) s_next = min(c_begin + kAhead * kWaves, c_end);
     for (int e = tid; e < (2 + p.rw) * W; e += kThreads)
         (e < 2 * W ? part[e] : wcnt[e - 2 * W]) = 0;
     __syncthreads();
@@ -257,45 +269,59 @@ void layout_dispatch_persistent_kernel(PersistParams p) {
     }
     __syncthreads();
 
-    // 4. Stores, in rounds of kRound chunks per wave: wait for everything in
-    // flight, issue the loads of round r + kLead, store round r.  A wave's
-    // stores and loads count in one counter and may complete out of order,
-    // so a load can only be waited for together with the stores issued
-    // before it; the rounds bound that wait and keep row loads in flight
-    // while the stores drain.
-    auto store_chunk = [&](int i) {
-        const int c = cbase + i * kWaves;
-        if (i < p.Q && c < c_end) {
-            const int t = c / p.C;
-            const int v = min((c - t * p.C) * kWave + lane, p.nvec - 1);
-            const int32_t* sl = s_slot + (t - tA) * kp;
-            u32x4* dst = p.recv_x + v;
-            if (K > 0) {
-                int32_t slot[K > 0 ? K : 1];
+    // 4. Stores.  Each step waits for everything the wave has in flight,
+    // takes the next chunk of the run (if any is left) into the slot freed
+    // by the previous step and issues its load, then stores the oldest held
+    // chunk to its token's receive rows.  A wave's stores and loads count
+    // in one counter and may complete out of order, so a load can only be
+    // waited for together with the stores issued before it; holding kAhead
+    // chunks keeps row loads in flight while the stores drain.
+    auto store_chunk = [&](int c, const u32x4& data) {
+        const int t = c / p.C;
+        const int v = min((c - t * p.C) * kWave + lane, p.nvec - 1);
+        const int32_t* sl = s_slot + (t - tA) * kp;
+        u32x4* dst = p.recv_x + v;
+        if (K > 0) {
+            int32_t slot[K > 0 ? K : 1];
 #pragma unroll
-                for (int j = 0; j < K; ++j) slot[j] = __builtin_amdgcn_readfirstlane(sl[j]);
+            for (int j = 0; j < K; ++j) slot[j] = __builtin_amdgcn_readfirstlane(sl[j]);
 #pragma unroll
-                for (int j = 0; j < K; ++j)
-                    if (slot[j] >= 0 && slot[j] < p.R)
-                        __builtin_nontemporal_store(buf[i], dst + static_cast<int64_t>(slot[j]) * p.nvec);
-            } else {
-                for (int j = 0; j < k; ++j) {
-                    const int32_t slot = __builtin_amdgcn_readfirstlane(sl[j]);
-                    if (slot >= 0 && slot < p.R)
-                        __builtin_nontemporal_store(buf[i], dst + static_cast<int64_t>(slot) * p.nvec);
-                }
+            for (int j = 0; j < K; ++j)
+                if (slot[j] >= 0 && slot[j] < p.R)
+                    __builtin_nontemporal_store(data, dst + static_cast<int64_t>(slot[j]) * p.nvec);
+        } else {
+            for (int j = 0; j < k; ++j) {
+                const int32_t slot = __builtin_amdgcn_readfirstlane(sl[j]);
+                if (slot >= 0 && slot < p.R)
+                    __builtin_nontemporal_store(data, dst + static_cast<int64_t>(slot) * p.nvec);
             }
         }
     };
+    bool more = true;  // the run may still have chunks to hand out
+    for (;;) {
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-        if (r + kLead < kRounds) {
-#pragma unroll
-            for (int i = 0; i < kRound; ++i) load_chunk((r + kLead) * kRound + i);
+        for (int u = 0; u < kRing; ++u) {
+            const int sst = u;                        // slot stored in this step
+            const int sld = (u + kAhead) % kRing;     // slot stored in the previous step
+            __builtin_amdgcn_s_waitcnt(0x0f70);       // vmcnt(0)
+            int c_new = -1;
+            if (more) {
+                int got = 0;
+                if (lane == 0) got = atomicAdd(&s_next, 1);
+                c_new = __builtin_amdgcn_readfirstlane(got);
+                if (c_new >= c_end) {
+                    c_new = -1;
+                    more = false;
+                }
+            }
+            load_into(sld, c_new);
+            if (cid[sst] >= 0) store_chunk(cid[sst], buf[sst]);
+            cid[sst] = -1;
         }
+        bool held = false;
 #pragma unroll
-        for (int i = 0; i < kRound; ++i) store_chunk(r * kRound + i);
+        for (int s2 = 0; s2 < kRing; ++s2) held |= cid[s2] >= 0;
+        if (!more && !held) break;
     }
 }
 
