@@ -233,14 +233,14 @@ def fused_call_name(wl, ncu):
 def combine_kernel_name(wl, ncu):
     """The kernel ep_combine runs on this workload (the library's rule: the
     persistent form when every wave of one 1024-lane workgroup per CU gets at
-    least one 64-piece chunk and at most 16 launches of at most 14 chunks per
+    least one 64-piece chunk and at most 16 launches of at most 16 chunks per
     wave cover the batch)."""
     nvec = wl.H // 8
     C = -(-nvec // 64)
     nw = ncu * 16
     chunks = wl.T * C
-    launches = max(1, -(-chunks // (nw * 14)))
-    while -(-(-(-wl.T // launches) * C) // nw) > 14:
+    launches = max(1, -(-chunks // (nw * 16)))
+    while -(-(-(-wl.T // launches) * C) // nw) > 16:
         launches += 1
     if chunks >= nw and launches <= 16:
         return "combine_persistent_kernel"
