@@ -198,6 +198,69 @@ __device__ __forceinline__ u32x4 combine_piece(const u32x4* __restrict__ eo, int
     return r;
 }
 
+// The KB slots and weights of a token (scalar loads).  PIN: the values are
+// tied to this point by an empty asm, so that the loads are issued here --
+// under the row loads of the chunk before -- and not sunk by the compiler
+// to their first use, in front of the next chunk's row loads.
+template <int KB, bool PIN = false>
+__device__ __forceinline__ void load_entries(const int32_t* __restrict__ slots,
+                                             const float* __restrict__ w, int32_t (&s)[KB],
+                                             float (&wt)[KB]) {
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) {
+        s[jj] = slots[jj];
+        wt[jj] = w[jj];
+    }
+    if (PIN) {
+#pragma unroll
+        for (int jj = 0; jj < KB; ++jj) asm volatile("" : "+s"(s[jj]), "+s"(wt[jj]));
+    }
+}
+
+// combine_piece for k == KB with the token's slots and weights already in
+// hand (s, w): issues the KB row loads, runs `between` (which fetches the
+// next chunk's entries into s and w's successors), then the FMA chain.  On
+// return s and w hold what `between` fetched.
+template <int KB, typename Between>
+__device__ __forceinline__ u32x4 reduce_rows(const u32x4* __restrict__ eo, int nvec, int64_t R,
+                                             int v, int32_t (&s)[KB], float (&w)[KB],
+                                             Between between) {
+    bool ok[KB];
+    u32x4 buf[KB];
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) {
+        ok[jj] = s[jj] >= 0 && s[jj] < R;
+        buf[jj] = __builtin_nontemporal_load(eo + static_cast<int64_t>(ok[jj] ? s[jj] : 0) * nvec + v);
+    }
+    float wj[KB];
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) wj[jj] = w[jj];
+    between(s, w);
+    // all of the rows' loads (and the next entries' fetch) are issued before
+    // the first row is used
+    __builtin_amdgcn_sched_barrier(0);
+    float acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < KB; ++jj) {
+        const u32x4 p = buf[jj];
+        const float f[8] = {lo16(p.x), hi16(p.x), lo16(p.y), hi16(p.y),
+                            lo16(p.z), hi16(p.z), lo16(p.w), hi16(p.w)};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float a = __builtin_fmaf(wj[jj], f[c], acc[c]);
+            acc[c] = ok[jj] ? a : acc[c];
+        }
+    }
+    u32x4 r;
+    r.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+    r.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+    r.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
+    r.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+    return r;
+}
+
 // One workgroup per CU is four waves per SIMD; telling the compiler so lets
 // it keep all of a chunk's row loads in flight instead of trading them for
 // registers.
@@ -226,6 +289,15 @@ void combine_persistent_kernel(
     };
     u32x4 out[kHold];
     uint32_t dep = 0;
+    // k == KB: the slots and weights of the chunk about to be reduced,
+    // fetched one chunk ahead (a scalar load of them in front of every
+    // chunk's row loads was a dependent round trip per chunk)
+    int32_t sc[KB];
+    float wc[KB];
+    if (EXACT) {
+        const int64_t t0 = ps.t0 + min(base, ps.chunks - 1) / ps.C;
+        load_entries<KB>(slot_of + t0 * KB, weights + t0 * KB, sc, wc);
+    }
 #pragma unroll
     for (int i = 0; i < kHold; ++i) {
         // A SIMD issues for its oldest wave first, so with equal shares the
@@ -245,8 +317,18 @@ void combine_persistent_kernel(
             chunk_of(i, t, v);
             // this chunk's loads may not move above the previous result
             asm volatile("" : "+v"(v) : "v"(dep));
-            out[i] = combine_piece<KB, EXACT>(eo, nvec, k, slot_of + static_cast<int64_t>(t) * k,
-                                              weights + static_cast<int64_t>(t) * k, R, v);
+            if (EXACT) {
+                out[i] = reduce_rows<KB>(eo, nvec, R, v, sc, wc, [&](int32_t (&sn)[KB], float (&wn)[KB]) {
+                    // the next chunk's slots and weights, while this chunk's
+                    // rows load (the last chunk of a launch refetches its own)
+                    const int cn = min(base + (i + 1) * kPersistWaves, ps.chunks - 1);
+                    const int64_t tn = ps.t0 + cn / ps.C;
+                    load_entries<KB, true>(slot_of + tn * KB, weights + tn * KB, sn, wn);
+                });
+            } else {
+                out[i] = combine_piece<KB, EXACT>(eo, nvec, k, slot_of + static_cast<int64_t>(t) * k,
+                                                  weights + static_cast<int64_t>(t) * k, R, v);
+            }
             dep = out[i].x;
         }
     }
