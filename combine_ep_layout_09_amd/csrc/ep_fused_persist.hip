@@ -7,7 +7,13 @@
 //   offset[e] = #{valid ids below e}                    (exclusive scan of count)
 //   slot      = offset[e] + rank   (contiguous)
 //             = e*cap + rank if rank < cap, else -1     (fixed capacity)
-// and every entry with a slot receives a bit copy of token t's row.
+// and every entry with a slot receives a bit copy of token t's row.  As in
+// ep_layout.hip, the per-expert counts and expert-major receive rows follow
+// the dispatch code quoted in "[GH-ISSUE #282] Redundant atomics in
+// internode_ll", the order inside an expert the order consistency of
+// "[GH-ISSUE #18] Reasons for not calling NVSHMEM public APIs?", and a
+// token's payload the hidden data of "[PR #693] Pipeline direct NVLink
+// dispatch with triple-buffered prefetch" (Summary).
 //
 // Workgroup b owns a contiguous run of (token, 64-piece chunk) units -- 16 Q
 // of them, Q <= kHold -- and so a contiguous run of tokens [tA, tB).
