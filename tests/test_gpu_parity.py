@@ -530,16 +530,21 @@ def test_ue8m0_special_blocks(fused):
 
 @pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
 def test_non_default_stream(fused):
-    c = _random_case(333, 512, 4, 16, 0, True, seed=5, name="side_stream")
     s = torch.cuda.Stream()
+    c = _random_case(333, 512, 4, 16, 0, True, seed=5, name="side_stream")
+    check_case(c, run_gpu(c, stream=s, fused=fused))
+    # a prefill-sized bf16 batch (fused: the one-launch form; the persistent
+    # combine either way)
+    c = _random_case(2048, 2048, 8, 64, 0, False, seed=6, name="side_stream_prefill")
     check_case(c, run_gpu(c, stream=s, fused=fused))
 
 
 def test_fused_equals_separate_bitwise():
     """ep_layout_dispatch writes exactly what ep_layout + ep_dispatch write,
     receive rows and scales included, on the tiny and the decode workloads
-    (one-kernel path) and the prefill and skewed workloads (histogram kernel
-    plus ranking dispatch kernel)."""
+    (small-table kernel), the prefill workload (one launch of one workgroup
+    per CU) and the skewed workload (FP8 with k = 6: the layout kernels and
+    the dispatch kernel)."""
     for cid in (1, 2, 3, 4):
         c = Case.from_workload(workloads.make(cid))
         a = run_gpu(c)
@@ -549,10 +554,14 @@ def test_fused_equals_separate_bitwise():
                 assert np.array_equal(a[n].view(np.uint8), b[n].view(np.uint8)), (cid, n)
 
 
-def test_deterministic_reruns():
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+def test_deterministic_reruns(fused):
+    """Two runs give identical bits.  On the fused path at this size the
+    one-launch kernel hands chunks to whichever wave asks first, so which
+    wave stores a row differs from run to run; the bytes must not."""
     c = Case.from_workload(workloads.make(3))
-    a = run_gpu(c)
-    b = run_gpu(c)
+    a = run_gpu(c, fused=fused)
+    b = run_gpu(c, fused=fused)
     for n in a:
         if a[n] is not None:
             assert np.array_equal(a[n], b[n]), n
