@@ -8,6 +8,19 @@ namespace ep {
 
 constexpr int kWave = 64;
 
+// Immediate of s_waitcnt on gfx9-family ISAs, gfx950 included: vmcnt is split
+// over bits [3:0] (low four bits) and [15:14] (high two bits), expcnt is bits
+// [6:4] and lgkmcnt bits [11:8].  A field at its maximum (vmcnt 63, expcnt 7,
+// lgkmcnt 15) does not wait on that counter.
+constexpr unsigned waitcnt_imm(unsigned vmcnt, unsigned expcnt, unsigned lgkmcnt) {
+    return (vmcnt & 0xfu) | ((vmcnt >> 4) << 14) | ((expcnt & 0x7u) << 4) |
+           ((lgkmcnt & 0xfu) << 8);
+}
+// Wait until every vector memory operation of the wave has completed (loads
+// and stores share the counter); LDS, scalar and export counters untouched.
+constexpr unsigned kWaitVmcnt0 = waitcnt_imm(0, 7, 15);
+static_assert(kWaitVmcnt0 == 0x0f70u, "gfx9 s_waitcnt encoding of vmcnt(0)");
+
 // Lanes below this one in the wave.
 __device__ __forceinline__ uint64_t lanemask_lt() {
     const uint32_t lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));

@@ -14,11 +14,15 @@
 // launches and by the layout's chain of dependent memory round trips.  Here
 // no workgroup waits for another: every workgroup derives, from the whole
 // table staged in its LDS, exactly the slots it needs (ep_small_dev.h), while
-// its token rows load.  This follows the pages' low-latency design advice:
-// "[GH-ISSUE #18] Reasons for not calling NVSHMEM public APIs?" on keeping
-// synchronisation and atomics off the microsecond path, and "[GH-ISSUE #166]
-// Why does DeepEP LL kernel use double send/recv/signal buffers?" on folding
-// clean-up work into the communication kernel itself.  Workgroup b scatters
+// its token rows load.  Two maintainer answers on the pages bear on this:
+// in "[GH-ISSUE #18] Reasons for not calling NVSHMEM public APIs?" the sync
+// and atomic operations a general API performs are named as too costly for
+// microsecond-level latency (here: no workgroup waits for another), and in
+// "[GH-ISSUE #166] Why does DeepEP LL kernel use double send/recv/signal
+// buffers?" the clearing of the next buffer runs in parallel with the use of
+// the current one to save latency (here: the only clearing the layout needs,
+// marking unused receive rows, runs inside the same kernel, beside the row
+// stores, rather than as a pass of its own).  Workgroup b scatters
 // items 2b and 2b+1 (token, column tile), one per 128-lane group, as the
 // dispatch kernel does; its entries are the 2k entries of those two tokens.
 // Tile 0 of a token writes its slot_of and src_of_slot entries.  Workgroup b

@@ -311,7 +311,7 @@ void layout_dispatch_persistent_kernel(PersistParams p) {
         for (int u = 0; u < kRing; ++u) {
             const int sst = u;                        // slot stored in this step
             const int sld = (u + kAhead) % kRing;     // slot stored in the previous step
-            __builtin_amdgcn_s_waitcnt(0x0f70);       // vmcnt(0)
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // vmcnt(0)
             int c_new = -1;
             if (more) {
                 int got = 0;

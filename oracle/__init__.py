@@ -122,7 +122,28 @@ def layout(topk_idx, E, cap=0):
                 status=status)
 
 
-def dispatch(x_bf16, slot_of, R, use_fp8, recv_x=None, recv_scales=None, t0=0, t1=None):
+def _token_ranges(t0, t1, threads):
+    n = t1 - t0
+    parts = max(1, min(int(threads), n))
+    cuts = [t0 + (n * i) // parts for i in range(parts + 1)]
+    return [(cuts[i], cuts[i + 1]) for i in range(parts) if cuts[i + 1] > cuts[i]]
+
+
+def _run_ranges(fn, t0, t1, threads):
+    """Call fn(a, b) over a split of [t0, t1) into token ranges, in host
+    threads (ctypes releases the GIL during the C call).  Every token is
+    handled by exactly one call, and the oracle's per-token work does not
+    depend on the split, so the result equals one serial call."""
+    ranges = _token_ranges(t0, t1, threads)
+    if len(ranges) <= 1:
+        return [fn(t0, t1)]
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(len(ranges)) as ex:
+        return list(ex.map(lambda r: fn(*r), ranges))
+
+
+def dispatch(x_bf16, slot_of, R, use_fp8, recv_x=None, recv_scales=None, t0=0, t1=None,
+             threads=1):
     """Scatter (and optionally quantise) token rows into receive rows.
 
     use_fp8: 0 bf16 rows; 1 E4M3FN rows + fp32 scales [R, H/128]; 2 E4M3FN rows
@@ -130,6 +151,8 @@ def dispatch(x_bf16, slot_of, R, use_fp8, recv_x=None, recv_scales=None, t0=0, t
     x_bf16 uint16 [T, H]; slot_of int32 [T, k].  recv_x / recv_scales may be
     passed pre-filled (rows no entry maps to keep their contents); otherwise
     they are created filled with 0xFF bytes.  Returns (recv_x, recv_scales).
+    threads > 1 splits the tokens [t0, t1) over that many host threads (the
+    receive rows of different tokens are disjoint, so the result is the same).
     """
     x = _need(x_bf16, np.uint16)
     s = _need(slot_of, np.int32)
@@ -148,17 +171,22 @@ def dispatch(x_bf16, slot_of, R, use_fp8, recv_x=None, recv_scales=None, t0=0, t
     else:
         if recv_x is None:
             recv_x = np.full((R, H), 0xFFFF, np.uint16)
-    rc = _load().orc_dispatch(T, H, k, R, mode, t0, t1, _ptr(x), _ptr(s),
-                              _ptr(recv_x), _ptr(recv_scales) if mode else None)
-    if rc != 0:
+    lib = _load()
+
+    def part(a, b):
+        return lib.orc_dispatch(T, H, k, R, mode, a, b, _ptr(x), _ptr(s),
+                                _ptr(recv_x), _ptr(recv_scales) if mode else None)
+
+    if any(rc != 0 for rc in _run_ranges(part, t0, t1, threads)):
         raise ValueError("orc_dispatch rejected its arguments")
     return recv_x, (recv_scales if use_fp8 else None)
 
 
-def combine(expert_out_bf16, slot_of, topk_weights, t0=0, t1=None, want_acc=True):
+def combine(expert_out_bf16, slot_of, topk_weights, t0=0, t1=None, want_acc=True, threads=1):
     """Weighted gather-reduce.  Returns (y uint16 [T, H], acc float32 [T, H] or None).
 
-    Rows outside [t0, t1) of y / acc are left zero.
+    Rows outside [t0, t1) of y / acc are left zero.  threads > 1 splits the
+    tokens over that many host threads (each output row is one token's).
     """
     eo = _need(expert_out_bf16, np.uint16)
     s = _need(slot_of, np.int32)
@@ -168,7 +196,11 @@ def combine(expert_out_bf16, slot_of, topk_weights, t0=0, t1=None, want_acc=True
     t1 = T if t1 is None else t1
     y = np.zeros((T, H), np.uint16)
     acc = np.zeros((T, H), np.float32) if want_acc else None
-    rc = _load().orc_combine(T, H, k, R, t0, t1, _ptr(eo), _ptr(s), _ptr(w), _ptr(y), _ptr(acc))
-    if rc != 0:
+    lib = _load()
+
+    def part(a, b):
+        return lib.orc_combine(T, H, k, R, a, b, _ptr(eo), _ptr(s), _ptr(w), _ptr(y), _ptr(acc))
+
+    if any(rc != 0 for rc in _run_ranges(part, t0, t1, threads)):
         raise ValueError("orc_combine rejected its arguments")
     return y, acc

@@ -18,8 +18,11 @@ model:
              mean load, FP8, contiguous
 
 Random numbers come from numpy's PCG64, one independent substream per
-(seed, workload id, purpose).  Normal draws are fp32 and are rounded to bf16
-with torch's CPU conversion (round to nearest even).
+(seed, workload id, purpose); the two large normal arrays (hidden states and
+expert outputs) take one substream per block of 2048 rows as well, so that
+their blocks can be drawn by several host threads with the same result.
+Normal draws are fp32 and are rounded to bf16 with torch's CPU conversion
+(round to nearest even).
 
 bf16 arrays are returned as uint16 bit patterns; ids as int32; weights fp32.
 """
@@ -53,13 +56,51 @@ def to_bf16_bits(f32):
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
 
 
-def normal_bf16(rng, shape, chunk_rows=4096):
-    """N(0,1) bf16 bit patterns of the given 2-D shape, drawn row-chunk by row-chunk."""
+BLOCK_ROWS = 2048
+
+
+def _threads():
+    try:
+        import os
+        return max(1, min(16, len(os.sched_getaffinity(0))))
+    except (AttributeError, OSError):
+        return 4
+
+
+def normal_f32_blocks(seed, cid, tag, shape):
+    """N(0,1) fp32 array of the given 2-D shape; rows [b*2048, (b+1)*2048)
+    come from substream (seed, cid, tag, b).  Blocks are drawn in host
+    threads (numpy releases the GIL while it fills an array); the result does
+    not depend on the thread count."""
+    from concurrent.futures import ThreadPoolExecutor
+    rows, cols = shape
+    out = np.empty((rows, cols), np.float32)
+
+    def fill(b):
+        r0, r1 = b * BLOCK_ROWS, min(rows, (b + 1) * BLOCK_ROWS)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, cid, tag, b])))
+        out[r0:r1] = g.standard_normal((r1 - r0, cols), dtype=np.float32)
+
+    nblk = -(-rows // BLOCK_ROWS)
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range(nblk)))
+    return out
+
+
+def normal_bf16_blocks(seed, cid, tag, shape):
+    """bf16 bit patterns (uint16) of normal_f32_blocks, rounded block by block."""
+    from concurrent.futures import ThreadPoolExecutor
     rows, cols = shape
     out = np.empty((rows, cols), np.uint16)
-    for r0 in range(0, rows, chunk_rows):
-        r1 = min(rows, r0 + chunk_rows)
-        out[r0:r1] = to_bf16_bits(rng.standard_normal((r1 - r0, cols), dtype=np.float32))
+
+    def fill(b):
+        r0, r1 = b * BLOCK_ROWS, min(rows, (b + 1) * BLOCK_ROWS)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, cid, tag, b])))
+        out[r0:r1] = to_bf16_bits(g.standard_normal((r1 - r0, cols), dtype=np.float32))
+
+    nblk = -(-rows // BLOCK_ROWS)
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range(nblk)))
     return out
 
 
@@ -167,7 +208,7 @@ class Workload:
 
     def expert_out(self):
         """bf16 N(0,1) expert outputs [R, H] in the receive-row layout."""
-        return normal_bf16(_rng(self.seed, self.cid, _EOUT), (self.R, self.H))
+        return normal_bf16_blocks(self.seed, self.cid, _EOUT, (self.R, self.H))
 
     def describe(self):
         return dict(workload=self.name, config_id=self.cid, seed=self.seed, T=self.T,
@@ -183,7 +224,7 @@ def make(cid, seed=0, **overrides):
     T, H, E, k, cap, fp8 = (cfg[n] for n in ("T", "H", "E", "k", "cap", "fp8"))
     meta = {}
 
-    xf = _rng(seed, cid, _X).standard_normal((T, H), dtype=np.float32)
+    xf = normal_f32_blocks(seed, cid, _X, (T, H))
     if cfg.get("outlier_frac"):
         n_out = math.ceil(cfg["outlier_frac"] * T)
         rows = _rng(seed, cid, _OUTLIER).choice(T, size=n_out, replace=False) if T else []
