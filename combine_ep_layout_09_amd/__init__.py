@@ -13,6 +13,8 @@ Entry points (same names as the C ABI):
   ep_dispatch(prob, x, layout, recv_x, recv_scales=None, stream=None)
   ep_layout_dispatch(prob, topk_idx, layout, workspace, x, recv_x, recv_scales=None,
                      stream=None)
+  ep_layout_dispatch_noalloc(prob, topk_idx, layout, x, recv_x, recv_scales=None,
+                             stream=None)   (workspace: the library's device array)
   ep_combine(prob, expert_out, layout, topk_weights, y, stream=None)
   ep_e4m3_encode(inp, out, stream=None)
   ep_strerror(code)
@@ -32,7 +34,7 @@ __all__ = [
     "ep_layout", "ep_dispatch", "ep_combine", "ep_e4m3_encode", "ep_strerror",
     "alloc_workspace", "alloc_recv", "library_path", "load_library",
     "prepare_layout", "prepare_dispatch", "prepare_combine", "ep_layout_dispatch",
-    "prepare_layout_dispatch",
+    "prepare_layout_dispatch", "ep_layout_dispatch_noalloc",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -98,6 +100,8 @@ def load_library():
     lib.ep_dispatch.argtypes = [P, vp, L, vp, vp, vp]
     lib.ep_layout_dispatch.restype = ctypes.c_int
     lib.ep_layout_dispatch.argtypes = [P, vp, L, vp, ctypes.c_size_t, vp, vp, vp, vp]
+    lib.ep_layout_dispatch_noalloc.restype = ctypes.c_int
+    lib.ep_layout_dispatch_noalloc.argtypes = [P, vp, L, vp, vp, vp, vp]
     lib.ep_combine.restype = ctypes.c_int
     lib.ep_combine.argtypes = [P, vp, L, vp, vp, vp]
     lib.ep_e4m3_encode.restype = ctypes.c_int
@@ -268,6 +272,17 @@ def ep_layout_dispatch(prob, topk_idx, layout, workspace, x, recv_x, recv_scales
     lib = load_library()
     _s, args = _layout_dispatch_args(prob, topk_idx, layout, workspace, x, recv_x, recv_scales)
     _check("ep_layout_dispatch", lib.ep_layout_dispatch(*args, _stream_handle(stream)))
+
+
+def ep_layout_dispatch_noalloc(prob, topk_idx, layout, x, recv_x, recv_scales=None,
+                               stream=None):
+    """ep_layout_dispatch with the library's own fixed device array as the
+    workspace (nothing is allocated; calls that overlap on one GPU race)."""
+    lib = load_library()
+    _s, args = _layout_dispatch_args(prob, topk_idx, layout, None, x, recv_x, recv_scales)
+    pr, idx, s, _ws, _nbytes, xp, rp, sp = args
+    _check("ep_layout_dispatch_noalloc",
+           lib.ep_layout_dispatch_noalloc(pr, idx, s, xp, rp, sp, _stream_handle(stream)))
 
 
 def ep_combine(prob, expert_out, layout, topk_weights, y, stream=None):

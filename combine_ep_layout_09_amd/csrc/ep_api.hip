@@ -5,8 +5,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "ep.h"
 #include "ep_internal.h"
+
+// Device scratch of ep_layout_dispatch_noalloc: one copy per GPU (a file-scope
+// __device__ array exists once in every device's memory), held until the
+// process ends.  Host code never passes `scratch` itself to a kernel -- in
+// host code the name stands for a host-side shadow, not a device address --
+// but the pointer hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) int32_t scratch[ep::kMaxLayoutWorkspaceBytes / 4];
 
 namespace {
 
@@ -51,6 +60,49 @@ int check_layout_ptrs(const ep_problem& p, const ep_layout_t* lay, bool all) {
 }
 
 int from_hip(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices] = {};
+
+hipError_t scratch_address(void** out) {
+    int dev = -1;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_addr[dev] == nullptr) {
+        void* ptr = nullptr;
+        err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (ptr == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_addr[dev] = ptr;
+    }
+    *out = g_scratch_addr[dev];
+    return hipSuccess;
+}
+
+// Arguments of ep_layout_dispatch apart from the workspace.
+int check_layout_dispatch_args(const ep_problem* prob, const int32_t* topk_idx,
+                               const ep_layout_t* out, const void* x, void* recv_x,
+                               void* recv_scales) {
+    int rc = check_problem(prob);
+    if (rc != EP_OK) return rc;
+    rc = check_layout_ptrs(*prob, out, true);
+    if (rc != EP_OK) return rc;
+    if (static_cast<int64_t>(prob->num_tokens) * prob->num_topk > 0 && topk_idx == nullptr)
+        return EP_ERR_ARG;
+    if (!aligned16(topk_idx)) return EP_ERR_ALIGN;
+    if (prob->num_tokens > 0) {
+        if (x == nullptr || recv_x == nullptr) return EP_ERR_ARG;
+        if (prob->use_fp8 && recv_scales == nullptr) return EP_ERR_ARG;
+    }
+    if (!aligned16(x) || !aligned16(recv_x) || (prob->use_fp8 && !aligned16(recv_scales)))
+        return EP_ERR_ALIGN;
+    return EP_OK;
+}
 
 }  // namespace
 
@@ -103,27 +155,35 @@ int ep_dispatch(const ep_problem* prob, const void* x, const ep_layout_t* layout
 int ep_layout_dispatch(const ep_problem* prob, const int32_t* topk_idx, const ep_layout_t* out,
                        void* workspace, size_t workspace_bytes, const void* x, void* recv_x,
                        void* recv_scales, void* stream) {
-    int rc = check_problem(prob);
+    int rc = check_layout_dispatch_args(prob, topk_idx, out, x, recv_x, recv_scales);
     if (rc != EP_OK) return rc;
-    rc = check_layout_ptrs(*prob, out, true);
-    if (rc != EP_OK) return rc;
-    if (static_cast<int64_t>(prob->num_tokens) * prob->num_topk > 0 && topk_idx == nullptr)
-        return EP_ERR_ARG;
-    if (!aligned16(topk_idx)) return EP_ERR_ALIGN;
     if (workspace == nullptr ||
         static_cast<int64_t>(workspace_bytes) < ep::layout_workspace_bytes(*prob))
         return EP_ERR_ARG;
     if (!aligned16(workspace)) return EP_ERR_ALIGN;
-    if (prob->num_tokens > 0) {
-        if (x == nullptr || recv_x == nullptr) return EP_ERR_ARG;
-        if (prob->use_fp8 && recv_scales == nullptr) return EP_ERR_ARG;
-    }
-    if (!aligned16(x) || !aligned16(recv_x) || (prob->use_fp8 && !aligned16(recv_scales)))
-        return EP_ERR_ALIGN;
     return from_hip(ep::launch_layout_dispatch(*prob, topk_idx, *out, workspace, x, recv_x,
                                                prob->use_fp8 ? recv_scales : nullptr,
                                                static_cast<hipStream_t>(stream)));
 }
+
+int ep_layout_dispatch_noalloc(const ep_problem* prob, const int32_t* topk_idx,
+                               const ep_layout_t* out, const void* x, void* recv_x,
+                               void* recv_scales, void* stream) {
+    int rc = check_layout_dispatch_args(prob, topk_idx, out, x, recv_x, recv_scales);
+    if (rc != EP_OK) return rc;
+    if (ep::layout_workspace_bytes(*prob) > ep::kMaxLayoutWorkspaceBytes) return EP_ERR_UNSUPPORTED;
+    void* ws = nullptr;
+    const hipError_t err = scratch_address(&ws);
+    if (err != hipSuccess) return EP_ERR_HIP;
+    // The workspace needs no initialisation (the histogram kernel writes every
+    // word it later reads), so the array's previous contents do not matter.
+    return from_hip(ep::launch_layout_dispatch(*prob, topk_idx, *out, ws, x, recv_x,
+                                               prob->use_fp8 ? recv_scales : nullptr,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+static_assert(EP_NOALLOC_SCRATCH_BYTES == ep::kMaxLayoutWorkspaceBytes,
+              "ep.h states the size of the allocation-free entry point's device array");
 
 int ep_combine(const ep_problem* prob, const void* expert_out, const ep_layout_t* layout,
                const float* topk_weights, void* y, void* stream) {

@@ -40,6 +40,11 @@ LayoutGeometry layout_geometry(const ep_problem& p);
 LayoutGeometry layout_geometry_two_pass(const ep_problem& p);
 int64_t layout_workspace_bytes(const ep_problem& p);
 
+// Largest layout workspace of any supported problem (E = kMaxExperts): two
+// tables of 64 rows by (E + 1) int32, rounded up to 256 bytes.  The
+// allocation-free entry point keeps a device array of this size.
+constexpr int64_t kMaxLayoutWorkspaceBytes = ((2 * 64 * (kMaxExperts + 1) * 4 + 255) / 256) * 256;
+
 // Small routing tables (T*k entries): ep_layout and ep_layout_dispatch handle
 // them in one kernel in which every workgroup reads the whole table, as long
 // as the id visits of all workgroups together stay below kFusedMaxVisits.

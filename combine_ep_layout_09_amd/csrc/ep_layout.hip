@@ -141,6 +141,7 @@ int64_t layout_workspace_bytes(const ep_problem& p) {
     const int64_t bytes = 2 * static_cast<int64_t>(kTableStride) * (p.num_experts + 1) * 4;
     return ((bytes + 255) / 256) * 256;
 }
+static_assert(kTableStride == 64, "kMaxLayoutWorkspaceBytes assumes 64-row table columns");
 
 hipError_t launch_layout_tables(const ep_problem& p, const int32_t* topk_idx,
                                 const LayoutGeometry& g, int32_t* workspace, int32_t* status,

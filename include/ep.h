@@ -50,7 +50,9 @@
  * Ownership.  The caller allocates and owns every buffer, including the
  * layout workspace.  The library never allocates, frees, or keeps a pointer
  * after a call returns, and keeps no mutable global state: calls are
- * re-entrant and may be issued from several host threads.
+ * re-entrant and may be issued from several host threads.  The one exception
+ * is ep_layout_dispatch_noalloc, whose workspace is a fixed device array of
+ * the library (one per GPU; see its declaration).
  *
  * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
  * stream).  Every call only enqueues work; nothing synchronises.  Outputs are
@@ -176,6 +178,29 @@ int ep_dispatch(const ep_problem* prob, const void* x, const ep_layout_t* layout
 int ep_layout_dispatch(const ep_problem* prob, const int32_t* topk_idx, const ep_layout_t* out,
                        void* workspace, size_t workspace_bytes, const void* x, void* recv_x,
                        void* recv_scales, void* stream);
+
+/* Layout and dispatch as ep_layout_dispatch, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, results and errors are those
+ * of ep_layout_dispatch without the workspace: the workspace is a fixed
+ * device array of EP_NOALLOC_SCRATCH_BYTES bytes inside the library, one
+ * copy per GPU, held until the process ends.  The call itself allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine); its first
+ * call on a device looks the array's address up once (hipGetSymbolAddress)
+ * with that device current.
+ * Limit: the workspace of the problem must fit the array; every problem
+ * inside the supported envelope does (E <= 1024), and a larger one would be
+ * rejected with EP_ERR_UNSUPPORTED.  EP_ERR_HIP if the address lookup fails.
+ * Sharing: every call on one GPU uses that GPU's array, which keeps the last
+ * call's contents.  Nothing in it needs to start at zero (each call writes
+ * every word it reads before reading it), but two calls that overlap in time
+ * on one GPU (different streams, or different host threads without stream
+ * order between them) race on the array and give undefined results; order
+ * them on one stream. */
+#define EP_NOALLOC_SCRATCH_BYTES 524800
+int ep_layout_dispatch_noalloc(const ep_problem* prob, const int32_t* topk_idx,
+                               const ep_layout_t* out, const void* x, void* recv_x,
+                               void* recv_scales, void* stream);
 
 /* Combine: y[t][c] = bf16_RNE( fixed-order fused multiply-add chain over
  * j = 0..k-1 with slot_of[t*k+j] >= 0 of topk_weights[t*k+j] *

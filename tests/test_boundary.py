@@ -25,7 +25,7 @@ def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"ep_layout", "ep_dispatch", "ep_combine", "ep_num_recv_rows",
             "ep_layout_workspace_bytes", "ep_strerror", "ep_e4m3_encode",
-            "ep_layout_dispatch"} <= set(names)
+            "ep_layout_dispatch", "ep_layout_dispatch_noalloc"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} declared in ep.h but not exported"
 
@@ -83,6 +83,8 @@ def test_bad_problems_rejected_everywhere(prob, code):
     assert lib.ep_combine(ctypes.byref(prob), FAKE, ctypes.byref(s), FAKE, FAKE, None) == code
     assert lib.ep_layout_dispatch(ctypes.byref(prob), FAKE, ctypes.byref(s), FAKE, 1 << 30, FAKE,
                                   FAKE, FAKE, None) == code
+    assert lib.ep_layout_dispatch_noalloc(ctypes.byref(prob), FAKE, ctypes.byref(s), FAKE, FAKE,
+                                          FAKE, None) == code
     assert lib.ep_num_recv_rows(ctypes.byref(prob)) == -1
     assert lib.ep_layout_workspace_bytes(ctypes.byref(prob)) == -1
 
@@ -126,6 +128,14 @@ def test_null_and_alignment_checks():
     assert LD(P, FAKE, S, FAKE, ws, FAKE + 8, FAKE, None, None) == ep.EP_ERR_ALIGN
     assert LD(ctypes.byref(p8), FAKE, S, FAKE, ws, FAKE, FAKE, None, None) == ep.EP_ERR_ARG
     assert LD(P, FAKE, ctypes.byref(_layout_struct(count=None)), FAKE, ws, FAKE, FAKE, None, None) == ep.EP_ERR_ARG
+    NA = lib.ep_layout_dispatch_noalloc
+    assert NA(P, None, S, FAKE, FAKE, None, None) == ep.EP_ERR_ARG
+    assert NA(P, FAKE + 4, S, FAKE, FAKE, None, None) == ep.EP_ERR_ALIGN
+    assert NA(P, FAKE, S, None, FAKE, None, None) == ep.EP_ERR_ARG
+    assert NA(P, FAKE, S, FAKE, None, None, None) == ep.EP_ERR_ARG
+    assert NA(P, FAKE, S, FAKE + 8, FAKE, None, None) == ep.EP_ERR_ALIGN
+    assert NA(ctypes.byref(p8), FAKE, S, FAKE, FAKE, None, None) == ep.EP_ERR_ARG
+    assert NA(P, FAKE, ctypes.byref(_layout_struct(count=None)), FAKE, FAKE, None, None) == ep.EP_ERR_ARG
     assert lib.ep_e4m3_encode(None, FAKE, 5, None) == ep.EP_ERR_ARG
     assert lib.ep_e4m3_encode(FAKE, FAKE, -1, None) == ep.EP_ERR_ARG
     assert lib.ep_e4m3_encode(FAKE + 1, FAKE, 5, None) == ep.EP_ERR_ALIGN
