@@ -16,11 +16,13 @@
 // dispatch with triple-buffered prefetch" (Summary).
 //
 // Workgroup b owns a contiguous run of (token, 64-piece chunk) units -- 16 Q
-// of them, Q <= kHold -- and so a contiguous run of tokens [tA, tB).
-// Nothing waits for another workgroup:
-//   1. every lane issues its first loads at once: the workgroup's own routing
-//      entries (one per lane), the whole routing table (kIdQuads quads per
-//      lane), then its wave's first kAhead row chunks;
+// of them, Q <= kHold -- and so a contiguous run of tokens [tA, tB); wave w
+// holds chunks w, w + 16, ... of the run.  Nothing waits for another
+// workgroup:
+//   1. every lane issues all of its loads at once: the workgroup's own
+//      routing entries (one per lane), the whole routing table (kIdQuads
+//      quads per lane), then all Q row chunks of its wave (kept in
+//      registers until they are stored);
 //   2. while the rows are in flight, the table builds two LDS histograms:
 //      the ids ahead of the workgroup's first entry, and the rest (the
 //      counting sort's "entries before i" split at the workgroup's start);
@@ -30,21 +32,27 @@
 //      an own entry's rank is the ids ahead of the workgroup with its
 //      expert, plus the own entries of earlier waves, plus the peers of
 //      lower lanes in its wave;
-//   4. every wave stores chunks to the k receive rows of their tokens one
-//      step at a time, loading a later chunk while a step's stores drain;
-//      past its first kAhead chunks a wave takes the run's next chunk from
-//      an LDS counter, so that the waves of a workgroup finish together.
+//   4. every wave waits once for its rows, then issues the stores of all of
+//      its chunks to the k receive rows of their tokens with no wait in
+//      between.  A wave's loads and stores share one counter and stores
+//      complete in any order, so a wait for a row load issued after a store
+//      also waits for that store; loading every row before the first store
+//      keeps the stores back to back, and with the caches flushed between
+//      calls the reads of x (at the start) and the writes (after it) no
+//      longer alternate on the HBM bus.  Measured at the 4096-token prefill
+//      with cold caches: 105-107 us against 110-111 us for a ring of four
+//      chunks loaded ahead of each store step.
 // Every workgroup builds the same whole-table histogram (a read of the table
 // from L2 per CU): the price of needing no other workgroup, paid while the
-// workgroup's first rows arrive from HBM.  Workgroup 0 writes count, offset
-// and status; the workgroup holding chunk 0 of a token writes its slot_of
-// and src_of_slot entries; receive rows that no entry fills are marked -1 by
+// workgroup's rows arrive from HBM.  Workgroup 0 writes count, offset and
+// status; the workgroup holding chunk 0 of a token writes its slot_of and
+// src_of_slot entries; receive rows that no entry fills are marked -1 by
 // workgroups in turn.
 //
-// Why: at the 4096-token prefill shape the two-launch form (a histogram
-// kernel, then a dispatch kernel that ranks each token) pays a kernel
-// boundary of about 4 us between the two; here the layout runs under the
-// first row loads of the same launch.
+// Why one launch: at the 4096-token prefill shape the two-launch form (a
+// histogram kernel, then a dispatch kernel that ranks each token) pays a
+// kernel boundary of about 4 us between the two; here the layout runs under
+// the row loads of the same launch.
 
 #include "ep_dispatch_dev.h"
 #include "ep_internal.h"
@@ -61,8 +69,6 @@ using layout::wave_inclusive_scan;
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kHold = 14;        // row chunks per wave of one launch, at most (Q)
-constexpr int kAhead = 4;        // chunks a wave has loaded ahead of its next store
-constexpr int kRing = kAhead + 1;
 constexpr int kIdQuads = 8;      // routing-table quads per lane (32 ids)
 constexpr int kMaxIds = 4 * kIdQuads * kThreads;  // routing entries (T*k) of this form
 constexpr size_t kMaxLds = 65536;
@@ -144,37 +150,27 @@ void layout_dispatch_persistent_kernel(PersistParams p) {
     int4 q[kIdQuads];
 #pragma unroll
     for (int u = 0; u < kIdQuads; ++u) q[u] = quads[min(u * kThreads + tid, nq - 1)];
-    // ... and the wave's first kAhead row chunks (chunks w, w + 16, ... of
-    // the workgroup's run), into a ring of kRing slots; cid[s] is the chunk
-    // slot s holds, -1 for none.  Every load is issued -- a slot with no chunk
-    // reads the run's last chunk again (a cache hit, never stored) -- because
-    // with loads under branches the compiler could no longer count which of
-    // them are still in flight, and the histogram below would wait for the
-    // rows instead of only for the table.
+    // ... and the wave's Q row chunks (chunks w, w + 16, ... of the
+    // workgroup's run, non-temporal: each is read once); cid[j] is the chunk
+    // buf[j] holds, -1 for none.  Every load is issued -- a slot with no
+    // chunk reads the run's last chunk again (a cache hit, never stored) --
+    // because with loads under branches the compiler could no longer count
+    // which of them are still in flight, and the histogram below would wait
+    // for the rows instead of only for the table.
     const int c_last = max(c_end - 1, 0);
-    u32x4 buf[kRing];
-    int cid[kRing];
-    auto load_into = [&](int s, int c) {
-        const int cc = c >= 0 ? c : c_last;
+    u32x4 buf[kHold];
+    int cid[kHold];
+#pragma unroll
+    for (int j = 0; j < kHold; ++j) {
+        const int c = c_begin + wave + j * kWaves;
+        const bool mine = j < p.Q && c < c_end;
+        const int cc = mine ? c : c_last;
         const int t = cc / p.C;
         const int v = min((cc - t * p.C) * kWave + lane, p.nvec - 1);
-        buf[s] = p.x[static_cast<int64_t>(t) * p.nvec + v];
-        cid[s] = c;
-    };
-#pragma unroll
-    for (int j = 0; j < kAhead; ++j) {
-        const int c = c_begin + wave + j * kWaves;
-        load_into(j, c < c_end ? c : -1);
+        buf[j] = __builtin_nontemporal_load(p.x + static_cast<int64_t>(t) * p.nvec + v);
+        cid[j] = mine ? c : -1;
     }
-    cid[kAhead] = -1;
 
-    // Chunks past the first kAhead of every wave are handed out in turn by an
-    // LDS counter, to whichever wave comes for one next: a SIMD issues for
-    // its oldest wave first, and with a fixed share per wave the youngest
-    // waves finished up to twice as late as the oldest (measured), leaving
-    // the end of the kernel to a quarter of the waves.
-    __shared__ int s_next;
-    if (tid == 0) s_next = min(c_begin + kAhead * kWaves, c_end);
     for (int e = tid; e < (2 + p.rw) * W; e += kThreads)
         (e < 2 * W ? part[e] : wcnt[e - 2 * W]) = 0;
     __syncthreads();
@@ -275,13 +271,8 @@ void layout_dispatch_persistent_kernel(PersistParams p) {
     }
     __syncthreads();
 
-    // 4. Stores.  Each step waits for everything the wave has in flight,
-    // takes the next chunk of the run (if any is left) into the slot freed
-    // by the previous step and issues its load, then stores the oldest held
-    // chunk to its token's receive rows.  A wave's stores and loads count
-    // in one counter and may complete out of order, so a load can only be
-    // waited for together with the stores issued before it; holding kAhead
-    // chunks keeps row loads in flight while the stores drain.
+    // 4. Stores: one wait for the rows, then every store of the wave with no
+    // wait in between.
     auto store_chunk = [&](int c, const u32x4& data) {
         const int t = c / p.C;
         const int v = min((c - t * p.C) * kWave + lane, p.nvec - 1);
@@ -303,45 +294,20 @@ void layout_dispatch_persistent_kernel(PersistParams p) {
             }
         }
     };
-    int steps = 0;     // chunks this wave has stored
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    // Issue priority falls from 3 to 0 over the quarters of a wave's chunks:
+    // a SIMD issues for its oldest wave first, and a wave ahead of the others
+    // yields the SIMD to them, as in the persistent combine.
     __builtin_amdgcn_s_setprio(3);
-    bool more = true;  // the run may still have chunks to hand out
-    for (;;) {
 #pragma unroll
-        for (int u = 0; u < kRing; ++u) {
-            const int sst = u;                        // slot stored in this step
-            const int sld = (u + kAhead) % kRing;     // slot stored in the previous step
-            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // vmcnt(0)
-            int c_new = -1;
-            if (more) {
-                int got = 0;
-                if (lane == 0) got = atomicAdd(&s_next, 1);
-                c_new = __builtin_amdgcn_readfirstlane(got);
-                if (c_new >= c_end) {
-                    c_new = -1;
-                    more = false;
-                }
-            }
-            load_into(sld, c_new);
-            if (cid[sst] >= 0) {
-                store_chunk(cid[sst], buf[sst]);
-                // Issue priority falls from 3 to 0 over the quarters of a
-                // wave's expected share (Q chunks), as in the persistent
-                // combine: a wave ahead of the others yields the SIMD to
-                // them (measured: 96.8 against 97.9-98.3 us at the
-                // 4096-token prefill).
-                const int level = (4 * ++steps) / p.Q;  // uniform
-                if (level == 0) __builtin_amdgcn_s_setprio(3);
-                else if (level == 1) __builtin_amdgcn_s_setprio(2);
-                else if (level == 2) __builtin_amdgcn_s_setprio(1);
-                else __builtin_amdgcn_s_setprio(0);
-            }
-            cid[sst] = -1;
+    for (int j = 0; j < kHold; ++j) {
+        if (cid[j] >= 0) {  // uniform
+            store_chunk(cid[j], buf[j]);
+            const int level = (4 * (j + 1)) / p.Q;
+            if (level == 1) __builtin_amdgcn_s_setprio(2);
+            else if (level == 2) __builtin_amdgcn_s_setprio(1);
+            else if (level >= 3) __builtin_amdgcn_s_setprio(0);
         }
-        bool held = false;
-#pragma unroll
-        for (int s2 = 0; s2 < kRing; ++s2) held |= cid[s2] >= 0;
-        if (!more && !held) break;
     }
 }
 
