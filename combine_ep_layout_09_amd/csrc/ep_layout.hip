@@ -90,6 +90,152 @@ __global__ __launch_bounds__(small::kThreads) void layout_small_kernel(
     small::fill_empty_rows(tab, E, cap, R, b, nwg, src_of_slot);
 }
 
+// ---- mid-size tables: one kernel, every workgroup reads the whole table ------
+//
+// Workgroup b ranks entries [1024 b, 1024 b + 1024), one per lane.  It needs,
+// per expert, the valid entries of the whole table (for the offsets) and
+// those before its first entry P0 (for the ranks): it reads the whole table
+// itself (served by L2 after the first workgroups of an XCD) and builds two
+// LDS histograms split at P0.  An own entry's rank is then the ids ahead of
+// P0 with its expert, plus the own entries of earlier waves with that expert
+// (per-wave counts), plus the lower lanes of its wave with that expert (one
+// ballot per key bit).  No workgroup waits for another; the one launch
+// replaces the histogram and ranking kernels of the two-pass path.
+
+constexpr int kWholeThreads = 1024;
+constexpr int kWholeWaves = kWholeThreads / kWave;
+constexpr int kWholeQuadSteps = 8;  // table quads a lane has in flight
+
+__host__ __device__ inline size_t whole_lds_words(int E) {
+    return static_cast<size_t>(3 + kWholeWaves) * (E + 1);
+}
+
+__global__ __launch_bounds__(kWholeThreads) void layout_whole_kernel(
+        const int32_t* __restrict__ idx, int n, int E, int cap, int64_t R, int nwg,
+        int32_t* __restrict__ count, int32_t* __restrict__ offset, int32_t* __restrict__ slot_of,
+        int32_t* __restrict__ src_of_slot, int32_t* __restrict__ status) {
+    extern __shared__ __align__(16) int32_t sm[];
+    __shared__ int32_t s_wsum[kWholeWaves];
+    __shared__ int32_t s_wover[kWholeWaves];
+    const int W = E + 1;
+    int32_t* part = sm;           // [2][E+1]: ids before P0, the rest (bin E: invalid)
+    int32_t* off = sm + 2 * W;    // [E+1]
+    int32_t* wcnt = off + W;      // [waves][E+1]: own entries per expert of each wave
+
+    const int tid = static_cast<int>(threadIdx.x);
+    const int lane = static_cast<int>(lane_id());
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int b = static_cast<int>(blockIdx.x);
+    const int P0 = b * kWholeThreads;
+    const int i_own = P0 + tid;
+    const bool has_own = i_own < n;
+    // the own entry first: a wave's loads return in issue order
+    const int32_t own_id = idx[has_own ? i_own : n - 1];
+    for (int e = tid; e < (2 + kWholeWaves) * W; e += kWholeThreads)
+        (e < 2 * W ? part[e] : wcnt[e - 2 * W]) = 0;
+    __syncthreads();
+
+    // Own entries: rank among the lower lanes of the wave, and per-wave
+    // counts (the lowest lane of each expert's peers records them).
+    const bool mine = has_own && valid_id(own_id, E);
+    const uint64_t peers = match_peers(static_cast<uint32_t>(mine ? own_id : 0), key_bits(E),
+                                       __ballot(mine));
+    const uint64_t lower = peers & lanemask_lt();
+    if (mine && lower == 0) wcnt[wave * W + own_id] = __popcll(peers);
+
+    // Histograms of the whole table, split at P0: kWholeQuadSteps 16-byte
+    // loads per lane in flight, then their counts.
+    const int nq = n / 4;
+    const int4* quads = reinterpret_cast<const int4*>(idx);
+    for (int q0 = 0; q0 < nq; q0 += kWholeQuadSteps * kWholeThreads) {
+        int4 g[kWholeQuadSteps];
+#pragma unroll
+        for (int u = 0; u < kWholeQuadSteps; ++u)
+            g[u] = quads[min(q0 + u * kWholeThreads + tid, nq - 1)];
+#pragma unroll
+        for (int u = 0; u < kWholeQuadSteps; ++u) {
+            const int qi = q0 + u * kWholeThreads + tid;
+            if (qi < nq) {
+                const int32_t id4[4] = {g[u].x, g[u].y, g[u].z, g[u].w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int32_t id = id4[c];
+                    atomicAdd(&part[(valid_id(id, E) ? id : E) + (4 * qi + c < P0 ? 0 : W)], 1);
+                }
+            }
+        }
+    }
+    if (tid < n - 4 * nq) {  // the last n % 4 ids
+        const int i = 4 * nq + tid;
+        const int32_t id = idx[i];
+        atomicAdd(&part[(valid_id(id, E) ? id : E) + (i < P0 ? 0 : W)], 1);
+    }
+    __syncthreads();
+
+    // Offsets: exclusive scan of the totals over experts (E <= 1024: one lane
+    // per expert), and the entries the capacity drops.
+    int32_t tot = 0, over = 0;
+    if (tid < E) {
+        tot = part[tid] + part[W + tid];
+        over = (cap > 0 && tot > cap) ? tot - cap : 0;
+    }
+    const int32_t incl = wave_inclusive_scan(tot);
+    const int32_t oincl = wave_inclusive_scan(over);
+    if (lane == kWave - 1) {
+        s_wsum[wave] = incl;
+        s_wover[wave] = oincl;
+    }
+    __syncthreads();
+    int32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += s_wsum[w];
+    if (tid < E) {
+        off[tid] = before + incl - tot;
+        if (b == 0) {
+            count[tid] = tot;
+            offset[tid] = before + incl - tot;
+        }
+    }
+    if (tid == 0) {
+        int32_t valid = 0, drop = 0;
+        for (int w = 0; w < kWholeWaves; ++w) {
+            valid += s_wsum[w];
+            drop += s_wover[w];
+        }
+        off[E] = valid;
+        if (b == 0) {
+            offset[E] = valid;
+            status[0] = part[E] + part[W + E];
+            status[1] = drop;
+        }
+    }
+    __syncthreads();
+
+    if (has_own) {
+        int32_t slot = -1;
+        if (mine) {
+            int32_t r = part[own_id] + __popcll(lower);
+            for (int w = 0; w < wave; ++w) r += wcnt[w * W + own_id];
+            if (cap == 0) slot = off[own_id] + r;
+            else if (r < cap) slot = own_id * cap + r;
+        }
+        slot_of[i_own] = slot;
+        if (slot >= 0 && slot < R) src_of_slot[slot] = i_own;
+    }
+    // Receive rows no entry fills: past each expert's count (fixed capacity,
+    // experts b, b + nwg, ...), or past the valid entries (contiguous).
+    if (cap > 0) {
+        for (int e = b; e < E; e += nwg) {
+            int32_t* rows = src_of_slot + static_cast<int64_t>(e) * cap;
+            const int32_t filled = min(part[e] + part[W + e], cap);
+            for (int r = filled + tid; r < cap; r += kWholeThreads) rows[r] = -1;
+        }
+    } else {
+        for (int64_t r = off[E] + static_cast<int64_t>(b) * kWholeThreads + tid; r < R;
+             r += static_cast<int64_t>(nwg) * kWholeThreads)
+            src_of_slot[r] = -1;
+    }
+}
+
 // ---- two-pass path -----------------------------------------------------------
 
 template <bool PREFIX>
@@ -143,6 +289,19 @@ int64_t layout_workspace_bytes(const ep_problem& p) {
 }
 static_assert(kTableStride == 64, "kMaxLayoutWorkspaceBytes assumes 64-row table columns");
 
+bool layout_whole_fits(const ep_problem& p) {
+    const int64_t n = static_cast<int64_t>(p.num_tokens) * p.num_topk;
+    // Few experts put many lanes of one LDS atomic instruction on the same
+    // histogram bin (more so with skewed routing), and every workgroup counts
+    // the whole table: below 128 experts, and past 65536 entries, the
+    // histogram and ranking kernels are faster (measured: the skewed
+    // 8192 x 6 table over 64 experts, 12.5 us against 4.6 + 5.6 us; 16384 x 8
+    // over 256 experts, about 16 against 15 us; 4096 x 8 over 256 experts,
+    // about 8 against 12 us, event-timed).
+    return n > kFusedMaxEntries && n <= kWholeMaxEntries && p.num_experts >= kWholeMinExperts &&
+           whole_lds_words(p.num_experts) * 4 <= 65536;
+}
+
 hipError_t launch_layout_tables(const ep_problem& p, const int32_t* topk_idx,
                                 const LayoutGeometry& g, int32_t* workspace, int32_t* status,
                                 hipStream_t stream) {
@@ -164,6 +323,14 @@ hipError_t launch_layout(const ep_problem& p, const int32_t* topk_idx, const ep_
         const int nwg = n > 0 ? (n + small::kMaxEntries - 1) / small::kMaxEntries : 1;
         hipLaunchKernelGGL(layout_small_kernel, dim3(nwg), dim3(small::kThreads),
                            small::lds_bytes(n, E), stream, topk_idx, n, E, p.capacity, R, nwg,
+                           out.count, out.offset, out.slot_of, out.src_of_slot, out.status);
+        return hipGetLastError();
+    }
+    if (layout_whole_fits(p)) {
+        const int n = static_cast<int>(g.entries);
+        const int nwg = (n + kWholeThreads - 1) / kWholeThreads;
+        hipLaunchKernelGGL(layout_whole_kernel, dim3(nwg), dim3(kWholeThreads),
+                           whole_lds_words(E) * 4, stream, topk_idx, n, E, p.capacity, R, nwg,
                            out.count, out.offset, out.slot_of, out.src_of_slot, out.status);
         return hipGetLastError();
     }

@@ -366,6 +366,32 @@ def test_duplicate_and_invalid_ids_large_table():
         assert got["status"][0] == int(((ids < 0) | (ids >= E)).sum())
 
 
+def test_whole_table_layout_ids_and_tails():
+    """The one-kernel layout of mid-size tables (8192 < T*k <= 65536, at
+    least 128 experts: every workgroup reads the whole table) through
+    ep_layout: duplicate ids in a row, ids outside [0, E), a run of one
+    expert across tokens, tokens without a valid entry, with and without
+    capacity (overflow included), tables whose length is not a multiple of 4
+    (the last ids are read one by one), and the same id mix on a larger
+    table that takes the two-kernel layout."""
+    rng = np.random.default_rng(12)
+    for T, k, E, cap in ((3000, 8, 160, 0), (3000, 8, 160, 100), (3001, 7, 130, 0),
+                         (4681, 14, 256, 0), (16384, 8, 256, 600)):
+        ids = rng.integers(0, E, size=(T, k))
+        ids[::7, 1] = ids[::7, 0]
+        ids[::11, 2] = -1
+        ids[::13, 3] = E
+        ids[::17, 0] = 1 << 30
+        ids[100:140] = 5
+        ids[200:203] = -1
+        H = 128 if T * k > 65536 else 256
+        c = _random_case(T, H, k, E, cap, False, seed=T + cap, ids=ids,
+                         name=f"whole_layout_T{T}_k{k}_E{E}_cap{cap}")
+        got = run_gpu(c)
+        check_case(c, got)
+        assert got["status"][0] == int(((ids < 0) | (ids >= E)).sum())
+
+
 def _fp8_special_xf(rng, T, H):
     """fp32 rows (T >= 6) whose first six rows hold the special FP8 cases."""
     xf = rng.standard_normal((T, H)).astype(np.float32)
