@@ -52,6 +52,19 @@ struct Bf16Tile {
             for (int u = 0; u < VPL; ++u) __builtin_nontemporal_store(buf[u], dst + v[u]);
         }
     }
+
+    // The same with the k <= 32 slots held one per lane (lane j: slot j), so
+    // that they come from one LDS read instead of k dependent ones.
+    __device__ __forceinline__ void store_lanes(int32_t slot_vec, int k, int64_t R,
+                                                u32x4* __restrict__ recv, int nvec) const {
+        for (int j = 0; j < k; ++j) {
+            const int32_t slot = __builtin_amdgcn_readlane(slot_vec, j);
+            if (slot < 0 || slot >= R) continue;
+            u32x4* dst = recv + static_cast<int64_t>(slot) * nvec;
+#pragma unroll
+            for (int u = 0; u < VPL; ++u) __builtin_nontemporal_store(buf[u], dst + v[u]);
+        }
+    }
 };
 
 // Maximum across the 16 lanes of a DPP row (all lanes get the result), for
@@ -209,6 +222,18 @@ struct Fp8Tile {
                                           u32x2* __restrict__ recv_q, int nvec) const {
         for (int j = 0; j < k; ++j) {
             const int32_t slot = __builtin_amdgcn_readfirstlane(slots[j]);
+            if (slot < 0 || slot >= R) continue;
+            u32x2* dst = recv_q + static_cast<int64_t>(slot) * nvec;
+#pragma unroll
+            for (int u = 0; u < VPL; ++u) __builtin_nontemporal_store(q[u], dst + v[u]);
+        }
+    }
+
+    // With the k <= 32 slots held one per lane (lane j: slot j).
+    __device__ __forceinline__ void store_lanes(int32_t slot_vec, int k, int64_t R,
+                                                u32x2* __restrict__ recv_q, int nvec) const {
+        for (int j = 0; j < k; ++j) {
+            const int32_t slot = __builtin_amdgcn_readlane(slot_vec, j);
             if (slot < 0 || slot >= R) continue;
             u32x2* dst = recv_q + static_cast<int64_t>(slot) * nvec;
 #pragma unroll

@@ -136,7 +136,11 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_small_kernel(SmallPa
         const int gq = tid / k;
         if (live[gq]) small::mark_entry(tab, E, tid, tab.ids[start[gq] + (tid - gq * k)]);
     }
-    small::histogram(tab, p.n, E);
+    // count, offset and status come from workgroup 0; with fixed capacity the
+    // others need neither offsets nor the whole histogram
+    const bool totals = p.cap == 0 || b == 0;
+    if (totals) small::histogram(tab, p.n, E);
+    else small::count_experts(tab, p.n, E, b, p.nwg);
     __syncthreads();
 
     // Equal ids ahead of each entry, up to the last entry of the later token.
@@ -152,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_small_kernel(SmallPa
         return m;
     };
     small::count_ahead(tab, end, E, ahead, s_eq);
-    small::scan_offsets(tab, E, p.cap, &s_drop);
+    if (totals) small::scan_offsets(tab, E, p.cap, &s_drop);
     if (FP8 && active) ft.quantise(p.nvec, tile, kGroupThreads, gtid, s_scale[g]);
     __syncthreads();
 
@@ -170,8 +174,9 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_small_kernel(SmallPa
 
     if (active) {
         const int32_t* slots = s_slot[g];
+        const int32_t slot_vec = (lane_id() < static_cast<uint32_t>(k)) ? slots[lane_id()] : -1;
         if (FP8) {
-            ft.store(slots, k, p.R, static_cast<u32x2*>(p.recv_x), p.nvec);
+            ft.store_lanes(slot_vec, k, p.R, static_cast<u32x2*>(p.recv_x), p.nvec);
             if (MODE == 2)
                 dispatch::fp8_store_scales(s_scale[g], slots, k, p.R,
                                            static_cast<uint8_t*>(p.recv_scales), p.nvec / 16,
@@ -181,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_small_kernel(SmallPa
                                            static_cast<float*>(p.recv_scales), p.nvec / 16, tile,
                                            kGroupThreads, VPL, gtid);
         } else {
-            bt.store(slots, k, p.R, static_cast<u32x4*>(p.recv_x), p.nvec);
+            bt.store_lanes(slot_vec, k, p.R, static_cast<u32x4*>(p.recv_x), p.nvec);
         }
     }
     small::fill_empty_rows(tab, E, p.cap, p.R, b, p.nwg, p.src_of_slot);
@@ -379,8 +384,9 @@ __global__ __launch_bounds__(1024) void layout_dispatch_ranked_kernel(RankedPara
     else bt.load(p.x, p.nvec, t, tile, nth, tid);
     __syncthreads();
 
+    const int32_t slot_vec = (lane < static_cast<uint32_t>(k)) ? s_slot[lane] : -1;
     if (FP8) {
-        ft.store(s_slot, k, p.R, static_cast<u32x2*>(p.recv_x), p.nvec);
+        ft.store_lanes(slot_vec, k, p.R, static_cast<u32x2*>(p.recv_x), p.nvec);
         if (MODE == 2)
             dispatch::fp8_store_scales(s_scale, s_slot, k, p.R,
                                        static_cast<uint8_t*>(p.recv_scales), p.nvec / 16, tile,
@@ -389,7 +395,7 @@ __global__ __launch_bounds__(1024) void layout_dispatch_ranked_kernel(RankedPara
             dispatch::fp8_store_scales(s_scale, s_slot, k, p.R, static_cast<float*>(p.recv_scales),
                                        p.nvec / 16, tile, nth, VPL, tid);
     } else {
-        bt.store(s_slot, k, p.R, static_cast<u32x4*>(p.recv_x), p.nvec);
+        bt.store_lanes(slot_vec, k, p.R, static_cast<u32x4*>(p.recv_x), p.nvec);
     }
 
     // Column totals, the layout's per-expert outputs and the empty rows.

@@ -68,7 +68,11 @@ __global__ __launch_bounds__(small::kThreads) void layout_small_kernel(
     __syncthreads();
 
     if (tid < cnt) small::mark_entry(tab, E, tid, tab.ids[a + tid]);
-    small::histogram(tab, n, E);
+    // count, offset and status come from workgroup 0; with fixed capacity the
+    // others need neither offsets nor the whole histogram
+    const bool totals = cap == 0 || b == 0;
+    if (totals) small::histogram(tab, n, E);
+    else small::count_experts(tab, n, E, b, nwg);
     __syncthreads();
 
     // Entry q sits at position a + q: an id at position i is ahead of the
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(small::kThreads) void layout_small_kernel(
         return (i < a) ? all : (all & (~0ull << (i - a + 1)));
     };
     small::count_ahead(tab, cnt > 0 ? a + cnt - 1 : 0, E, ahead, s_eq);
-    small::scan_offsets(tab, E, cap, &s_drop);
+    if (totals) small::scan_offsets(tab, E, cap, &s_drop);
     __syncthreads();
 
     if (tid < cnt) {

@@ -109,6 +109,20 @@ __device__ inline void histogram(const Tables& t, int n, int E) {
     }
 }
 
+// With fixed capacity a workgroup other than workgroup 0 needs no offsets
+// (its slots are e*cap + rank) and, of the histogram, only the counts of the
+// experts whose empty rows it marks (b, b + nwg, ...): those are counted
+// here, one wave sum and one LDS add per wave and expert, into hist (zeroed
+// by the caller before a barrier).
+__device__ inline void count_experts(const Tables& t, int n, int E, int b, int nwg) {
+    for (int e = b; e < E; e += nwg) {
+        int32_t c = 0;
+        for (int i = threadIdx.x; i < n; i += kThreads) c += (t.ids[i] == e) ? 1 : 0;
+        c = wave_inclusive_scan(c);
+        if (lane_id() == kWave - 1 && c != 0) atomicAdd(&t.hist[e], c);
+    }
+}
+
 // Adds, for every id at position i < end, one to eq[q] for each entry q in
 // map[id] & ahead(i), where ahead(i) is the mask of entries after position
 // i.  eq is LDS, zeroed by the caller before a barrier.
