@@ -249,6 +249,7 @@ FUSED_SOURCES = {
     "layout_dispatch_persistent_kernel": ("ep_fused_persist.hip",),
     "layout_hist_kernel+layout_dispatch_ranked_kernel": ("ep_fused.hip", "ep_layout.hip"),
     "layout_hist_kernel+layout_rank_kernel+dispatch_fp8_kernel": ("ep_layout.hip", "ep_dispatch.hip"),
+    "layout_whole_kernel+dispatch_fp8_kernel": ("ep_layout.hip", "ep_dispatch.hip"),
 }
 
 
@@ -257,14 +258,24 @@ def fused_call_name(wl, ncu):
     library's rule: one kernel for small tables; one persistent kernel for
     prefill-sized bf16 tables that fit it; the histogram kernel and the
     ranking dispatch kernel for other bf16 rows or k >= 8; otherwise the
-    layout kernels and the dispatch kernel)."""
+    layout kernel(s) and the dispatch kernel)."""
     if one_launch(wl):
         return "layout_dispatch_small_kernel"
     if persistent_launch(wl, ncu):
         return "layout_dispatch_persistent_kernel"
     if not wl.fp8 or wl.k >= 8:
         return "layout_hist_kernel+layout_dispatch_ranked_kernel"
+    if whole_table_layout(wl):
+        return "layout_whole_kernel+dispatch_fp8_kernel"
     return "layout_hist_kernel+layout_rank_kernel+dispatch_fp8_kernel"
+
+
+def whole_table_layout(wl):
+    """Whether ep_layout takes its one-kernel form for mid-size tables (the
+    library's rule: 8192 < T*k <= 65536, at least 128 experts, and
+    19 (E + 1) int32 of LDS within 64 KiB)."""
+    n = wl.T * wl.k
+    return 8192 < n <= 65536 and wl.E >= 128 and 19 * (wl.E + 1) * 4 <= 65536
 
 
 def combine_kernel_name(wl, ncu):
