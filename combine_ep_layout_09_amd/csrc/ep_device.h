@@ -58,25 +58,29 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 // kept on zero.  Input must not be NaN.
 //   |v| >= 448            -> 0x7E (everything from 448 up rounds to 448 once
 //                            the format's top code is NaN and values saturate)
-//   2^-6 <= |v| < 448     -> normal codes: drop 20 of the 23 fraction bits with
-//                            round-half-even on the integer pattern, then move
-//                            the exponent bias from 127 to 7
-//   |v| < 2^-6            -> subnormal codes m * 2^-9: round |v| * 2^9 to the
-//                            nearest even integer (m = 8 is exactly 2^-6 = 0x08)
+//   2^-6 <= |v| < 448     -> normal codes (3 fraction bits, bias 7)
+//   |v| < 2^-6            -> subnormal codes m * 2^-9, m = |v| * 2^9 rounded
+//                            to the nearest even integer
+// gfx950's v_cvt_pk_fp8_f32 converts two fp32 values to OCP E4M3FN with
+// round-to-nearest-even, subnormals included, but gives NaN (0x7F) from 464
+// up; clamping the input to [-448, 448] first (v_med3_f32) leaves every code
+// below 448 as it is and gives 448 above.  Both are checked exhaustively
+// through ep_e4m3_encode: every finite binary32 against a library encoder and
+// the saturation rule.
+__device__ __forceinline__ float e4m3_clamp(float v) {
+    return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
+}
+
+// Codes of a, b, c, d in bytes 0..3 of one word.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3_rne(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), w, true);
+    return static_cast<uint32_t>(w);
+}
+
 __device__ __forceinline__ uint32_t f32_to_e4m3_rne(float v) {
-    const uint32_t u = __float_as_uint(v);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7fffffffu;
-    uint32_t code;
-    if (a >= 0x43e00000u) {
-        code = 0x7eu;
-    } else if (a >= 0x3c800000u) {
-        const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
-        code = (r >> 20) - (120u << 3);
-    } else {
-        code = static_cast<uint32_t>(__builtin_rintf(__uint_as_float(a) * 512.0f));
-    }
-    return sign | code;
+    const float c = e4m3_clamp(v);
+    return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false)) & 0xffu;
 }
 
 }  // namespace ep

@@ -99,32 +99,31 @@ __device__ __forceinline__ float row16_max(float m) {
 __device__ __forceinline__ u32x2 quant8(const u32x4& w, float scale) {
     const float f[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
                         bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
-    uint32_t code[8];
-    uint32_t exact = 0;  // channels that need the division
-    if (scale == 0.0f) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) code[i] = 0;
-    } else {
-        const float r = 1.0f / scale;
-        const bool r_ok = __float_as_uint(r) < 0x7f800000u;  // finite (r > 0)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float p = f[i] * r;
-            const uint32_t a = __float_as_uint(p) & 0x7fffffffu;
-            const int mid = static_cast<int>(a & 0xfffffu) - 0x80000;
-            const bool ok = r_ok && (a == 0 || (a >= 0x3c800000u && (mid > 8 || mid < -8)));
-            code[i] = f32_to_e4m3_rne(p);
-            exact |= ok ? 0u : (1u << i);
-        }
-        if (__ballot(exact != 0)) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (exact & (1u << i)) code[i] = f32_to_e4m3_rne(f[i] / scale);
-        }
-    }
     u32x2 q;
-    q.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-    q.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+    if (scale == 0.0f) {
+        q.x = 0;
+        q.y = 0;
+        return q;
+    }
+    const float r = 1.0f / scale;
+    const bool r_ok = __float_as_uint(r) < 0x7f800000u;  // finite (r > 0)
+    float p[8];
+    uint32_t exact = 0;  // channels that need the division
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        p[i] = f[i] * r;
+        const uint32_t a = __float_as_uint(p[i]) & 0x7fffffffu;
+        const int mid = static_cast<int>(a & 0xfffffu) - 0x80000;
+        const bool ok = r_ok && (a == 0 || (a >= 0x3c800000u && (mid > 8 || mid < -8)));
+        exact |= ok ? 0u : (1u << i);
+    }
+    if (__ballot(exact != 0)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (exact & (1u << i)) p[i] = f[i] / scale;
+    }
+    q.x = f32x4_to_e4m3_rne(p[0], p[1], p[2], p[3]);
+    q.y = f32x4_to_e4m3_rne(p[4], p[5], p[6], p[7]);
     return q;
 }
 
@@ -145,12 +144,9 @@ __device__ __forceinline__ int ue8m0_exponent(float amax) {
 __device__ __forceinline__ u32x2 quant8_pow2(const u32x4& w, float factor, bool zero_block) {
     const float f[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
                         bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
-    uint32_t code[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) code[i] = zero_block ? 0u : f32_to_e4m3_rne(f[i] * factor);
     u32x2 q;
-    q.x = code[0] | (code[1] << 8) | (code[2] << 16) | (code[3] << 24);
-    q.y = code[4] | (code[5] << 8) | (code[6] << 16) | (code[7] << 24);
+    q.x = zero_block ? 0u : f32x4_to_e4m3_rne(f[0] * factor, f[1] * factor, f[2] * factor, f[3] * factor);
+    q.y = zero_block ? 0u : f32x4_to_e4m3_rne(f[4] * factor, f[5] * factor, f[6] * factor, f[7] * factor);
     return q;
 }
 
