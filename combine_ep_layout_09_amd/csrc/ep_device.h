@@ -63,10 +63,10 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 //                            to the nearest even integer
 // gfx950's v_cvt_pk_fp8_f32 converts two fp32 values to OCP E4M3FN with
 // round-to-nearest-even, subnormals included, but gives NaN (0x7F) from 464
-// up; clamping the input to [-448, 448] first (v_med3_f32) leaves every code
-// below 448 as it is and gives 448 above.  Both are checked exhaustively
-// through ep_e4m3_encode: every finite binary32 against a library encoder and
-// the saturation rule.
+// (exclusive) up; clamping the input to [-448, 448] first (v_med3_f32)
+// leaves every code below 448 as it is and gives 448 above.  Both are checked
+// exhaustively through ep_e4m3_encode: every finite binary32 against a
+// library encoder and the saturation rule.
 __device__ __forceinline__ float e4m3_clamp(float v) {
     return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f);
 }
@@ -75,6 +75,14 @@ __device__ __forceinline__ float e4m3_clamp(float v) {
 __device__ __forceinline__ uint32_t f32x4_to_e4m3_rne(float a, float b, float c, float d) {
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(a), e4m3_clamp(b), 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(c), e4m3_clamp(d), w, true);
+    return static_cast<uint32_t>(w);
+}
+
+// The same for values known to lie in [-464, 464], with no clamp: the
+// conversion itself rounds 448 < |v| <= 464 to 448.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3_rne_le464(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return static_cast<uint32_t>(w);
 }
 

@@ -88,14 +88,18 @@ __device__ __forceinline__ float row16_max(float m) {
 //
 // Dividing every channel is the ALU cost of FP8 dispatch, so the quotients
 // come from one IEEE reciprocal per piece instead: r = fl(1 / scale) and
-// p = fl(f * r) carry two roundings of relative error <= 2^-24 each, so p is
-// within 3 ulps of fl(f / scale).  The code of a quotient of E4M3-normal size
-// (>= 2^-6) changes only where the quotient crosses a midpoint between two
-// E4M3 values, which in fp32 bits is low 20 bits == 0x80000; a zero quotient
-// is exact.  A channel whose p is a zero, or at least 2^-6 and more than 8
-// ulps from a midpoint, therefore has the code of p.  The others (near a
-// midpoint, below 2^-6, or r not finite because scale is tiny) are divided,
-// in a branch that a wave takes only when one of its lanes needs it.
+// p = fl(f * r) carry two roundings of relative error <= 2^-24 each, so p
+// lies within 3 * 2^-24 |f / scale| of q = fl(f / scale), inside the interval
+// [p (1 - 2^-21), p (1 + 2^-21)] even after the rounding of its two ends.
+// Round-to-nearest-even onto E4M3 is monotone in the value, so where both
+// ends of that interval have the same code, q has it too (this holds at
+// zero, where the interval is a point, and for fp32-subnormal quotients,
+// whose codes are all a signed zero).  Each word of four channels whose end
+// codes differ in some byte -- a quotient next to a rounding midpoint --
+// and every channel when r is not finite (scale tiny) take the division
+// instead, in a branch a wave enters only when one of its lanes needs it.
+// Every value encoded here is below 464 in magnitude (|f| <= 448 * scale, and
+// the ends exceed p by less than 2^-20 relative), so no clamp is needed.
 __device__ __forceinline__ u32x2 quant8(const u32x4& w, float scale) {
     const float f[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
                         bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
@@ -107,23 +111,28 @@ __device__ __forceinline__ u32x2 quant8(const u32x4& w, float scale) {
     }
     const float r = 1.0f / scale;
     const bool r_ok = __float_as_uint(r) < 0x7f800000u;  // finite (r > 0)
+    constexpr float kDown = 1.0f - 0x1p-21f;
+    constexpr float kUp = 1.0f + 0x1p-21f;
     float p[8];
-    uint32_t exact = 0;  // channels that need the division
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        p[i] = f[i] * r;
-        const uint32_t a = __float_as_uint(p[i]) & 0x7fffffffu;
-        const int mid = static_cast<int>(a & 0xfffffu) - 0x80000;
-        const bool ok = r_ok && (a == 0 || (a >= 0x3c800000u && (mid > 8 || mid < -8)));
-        exact |= ok ? 0u : (1u << i);
-    }
-    if (__ballot(exact != 0)) {
+    for (int i = 0; i < 8; ++i) p[i] = f[i] * r;
+    q.x = f32x4_to_e4m3_rne_le464(p[0], p[1], p[2], p[3]);
+    q.y = f32x4_to_e4m3_rne_le464(p[4], p[5], p[6], p[7]);
+    const uint32_t lo0 = f32x4_to_e4m3_rne_le464(p[0] * kDown, p[1] * kDown, p[2] * kDown, p[3] * kDown);
+    const uint32_t hi0 = f32x4_to_e4m3_rne_le464(p[0] * kUp, p[1] * kUp, p[2] * kUp, p[3] * kUp);
+    const uint32_t lo1 = f32x4_to_e4m3_rne_le464(p[4] * kDown, p[5] * kDown, p[6] * kDown, p[7] * kDown);
+    const uint32_t hi1 = f32x4_to_e4m3_rne_le464(p[4] * kUp, p[5] * kUp, p[6] * kUp, p[7] * kUp);
+    const uint32_t d0 = r_ok ? lo0 ^ hi0 : ~0u;  // nonzero byte: that channel divides
+    const uint32_t d1 = r_ok ? lo1 ^ hi1 : ~0u;
+    if (__ballot((d0 | d1) != 0)) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (exact & (1u << i)) p[i] = f[i] / scale;
+        for (int i = 0; i < 4; ++i) {
+            if ((d0 >> (8 * i)) & 0xffu) p[i] = f[i] / scale;
+            if ((d1 >> (8 * i)) & 0xffu) p[4 + i] = f[4 + i] / scale;
+        }
+        q.x = f32x4_to_e4m3_rne_le464(p[0], p[1], p[2], p[3]);
+        q.y = f32x4_to_e4m3_rne_le464(p[4], p[5], p[6], p[7]);
     }
-    q.x = f32x4_to_e4m3_rne(p[0], p[1], p[2], p[3]);
-    q.y = f32x4_to_e4m3_rne(p[4], p[5], p[6], p[7]);
     return q;
 }
 
@@ -144,9 +153,9 @@ __device__ __forceinline__ int ue8m0_exponent(float amax) {
 __device__ __forceinline__ u32x2 quant8_pow2(const u32x4& w, float factor, bool zero_block) {
     const float f[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
                         bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
-    u32x2 q;
-    q.x = zero_block ? 0u : f32x4_to_e4m3_rne(f[0] * factor, f[1] * factor, f[2] * factor, f[3] * factor);
-    q.y = zero_block ? 0u : f32x4_to_e4m3_rne(f[4] * factor, f[5] * factor, f[6] * factor, f[7] * factor);
+    u32x2 q;  // |f * factor| <= 448: no clamp needed
+    q.x = zero_block ? 0u : f32x4_to_e4m3_rne_le464(f[0] * factor, f[1] * factor, f[2] * factor, f[3] * factor);
+    q.y = zero_block ? 0u : f32x4_to_e4m3_rne_le464(f[4] * factor, f[5] * factor, f[6] * factor, f[7] * factor);
     return q;
 }
 

@@ -533,7 +533,8 @@ hipError_t launch_layout_dispatch(const ep_problem& p, const int32_t* topk_idx,
             err = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
         if (err != hipSuccess) return err;
         if (layout_dispatch_persistent_fits(p, ncu))
-            return launch_layout_dispatch_persistent(p, topk_idx, out, x, recv_x, ncu, stream);
+            return launch_layout_dispatch_persistent(p, topk_idx, out, x, recv_x, recv_scales,
+                                                     ncu, stream);
         // Ranking inside the dispatch kernel puts two dependent round trips
         // (the token's ids, then its table columns) ahead of each
         // workgroup's row; that pays for bf16 rows and for FP8 with k >= 8,

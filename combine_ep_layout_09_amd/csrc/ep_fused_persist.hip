@@ -1,5 +1,6 @@
 // ep_fused_persist.hip -- ep_layout_dispatch for prefill-sized routing tables
-// and bf16 payloads in one launch of one 1024-lane workgroup per CU.
+// (8192 < T*k <= 32768) in one launch of one 1024-lane workgroup per CU, for
+// bf16 and FP8 payloads.
 //
 // The problem is the one of ep_layout followed by ep_dispatch.  For routing
 // entry i = t*k + j with valid expert e:
@@ -7,7 +8,8 @@
 //   offset[e] = #{valid ids below e}                    (exclusive scan of count)
 //   slot      = offset[e] + rank   (contiguous)
 //             = e*cap + rank if rank < cap, else -1     (fixed capacity)
-// and every entry with a slot receives a bit copy of token t's row.  As in
+// and every entry with a slot receives token t's row (a bit copy, or its
+// E4M3 codes and block scales as in ep_dispatch.hip).  As in
 // ep_layout.hip, the per-expert counts and expert-major receive rows follow
 // the dispatch code quoted in "[GH-ISSUE #282] Redundant atomics in
 // internode_ll", the order inside an expert the order consistency of
@@ -16,7 +18,8 @@
 // dispatch with triple-buffered prefetch" (Summary).
 //
 // Workgroup b owns a contiguous run of (token, 64-piece chunk) units -- 16 Q
-// of them, Q <= kHold -- and so a contiguous run of tokens [tA, tB); wave w
+// of them, Q <= kHold (bf16) or kHoldFp8 -- and so a contiguous run of tokens
+// [tA, tB); wave w
 // holds chunks w, w + 16, ... of the run.  Nothing waits for another
 // workgroup:
 //   1. every lane issues all of its loads at once: the workgroup's own
@@ -41,7 +44,9 @@
 //      calls the reads of x (at the start) and the writes (after it) no
 //      longer alternate on the HBM bus.  Measured at the 4096-token prefill
 //      with cold caches: 105-107 us against 110-111 us for a ring of four
-//      chunks loaded ahead of each store step.
+//      chunks loaded ahead of each store step.  FP8 rows are quantised
+//      chunk by chunk as they arrive, and each chunk is stored once it is
+//      quantised (see the FP8 kernel).
 // Every workgroup builds the same whole-table histogram (a read of the table
 // from L2 per CU): the price of needing no other workgroup, paid while the
 // workgroup's rows arrive from HBM.  Workgroup 0 writes count, offset and
@@ -61,6 +66,7 @@
 namespace ep {
 namespace {
 
+using dispatch::u32x2;
 using dispatch::u32x4;
 using layout::key_bits;
 using layout::valid_id;
@@ -68,7 +74,8 @@ using layout::wave_inclusive_scan;
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kHold = 14;        // row chunks per wave of one launch, at most (Q)
+constexpr int kHold = 14;        // bf16: row chunks per wave of one launch, at most (Q)
+constexpr int kHoldFp8 = 16;     // FP8: the same (quantised chunks take fewer registers)
 constexpr int kIdQuads = 8;      // routing-table quads per lane (32 ids)
 constexpr int kMaxIds = 4 * kIdQuads * kThreads;  // routing entries (T*k) of this form
 constexpr size_t kMaxLds = 65536;
@@ -84,10 +91,12 @@ struct PersistParams {
     int32_t* src_of_slot;
     int32_t* status;
     const u32x4* x;
-    u32x4* recv_x;
+    void* recv_x;       // bf16 rows (u32x4 pieces) or E4M3 rows (u32x2 pieces)
+    void* recv_scales;  // FP8: fp32 or UE8M0 block scales [R, nblk]
     int T, nvec;
+    int nblk;  // FP8: 128-channel blocks per row
     int C;     // 64-piece chunks per row
-    int Q;     // chunks per wave (<= kHold)
+    int Q;     // chunks per wave (<= kHold, kHoldFp8)
     int rw;    // waves that hold own entries: ceil(own entries / 64), <= kWaves
     int maxtok;  // tokens a workgroup touches, at most
     int nwg;
@@ -107,6 +116,172 @@ __host__ __device__ inline size_t persist_lds_words(int E, int rw, int maxtok, i
     return ((head + 3) & ~static_cast<size_t>(3)) + static_cast<size_t>(maxtok) * slot_stride(k);
 }
 
+// The workgroup's view of the problem: its run of chunks and tokens and its
+// LDS tables.
+struct Part {
+    int tid, lane, wave, b, E, k, kp, W;
+    int c_begin, c_end, tA, P0, n_own;
+    int32_t* part;
+    int32_t* off;
+    int32_t* wcnt;
+    int32_t* s_slot;
+};
+
+template <int K>
+__device__ __forceinline__ Part make_part(const PersistParams& p, int32_t* s_dyn) {
+    Part w;
+    w.tid = static_cast<int>(threadIdx.x);
+    w.lane = static_cast<int>(lane_id());
+    // the same for every lane of a wave: scalar from here on
+    w.wave = __builtin_amdgcn_readfirstlane(w.tid / kWave);
+    w.b = static_cast<int>(blockIdx.x);
+    w.E = p.E;
+    w.k = K > 0 ? K : p.k;
+    w.kp = slot_stride(w.k);
+    w.W = w.E + 1;
+    w.part = s_dyn;
+    w.off = w.part + 2 * w.W;
+    w.wcnt = w.off + w.W;
+    w.s_slot = s_dyn + ((static_cast<size_t>(3 + p.rw) * w.W + 3) & ~static_cast<size_t>(3));
+    const int all_chunks = p.T * p.C;  // < 2^31: at most CUs * 16 * kHoldFp8 here
+    w.c_begin = w.b * kWaves * p.Q;
+    w.c_end = min(w.c_begin + kWaves * p.Q, all_chunks);
+    const bool has = w.c_begin < w.c_end;
+    w.tA = has ? w.c_begin / p.C : 0;
+    const int tB = has ? (w.c_end - 1) / p.C + 1 : 0;
+    w.P0 = w.tA * w.k;             // the workgroup's first routing entry
+    w.n_own = (tB - w.tA) * w.k;   // <= rw * 64 (host-checked)
+    return w;
+}
+
+// Adds the 4 ids of table quad qi (quads past the end are not counted) to
+// the histogram of the ids ahead of the workgroup's first entry or to that
+// of the others.
+__device__ __forceinline__ void count_quad(const Part& w, int nq, const int4& g, int qi) {
+    if (qi < nq) {
+        const int32_t id4[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int32_t id = id4[c];
+            const int bin = (valid_id(id, w.E) ? id : w.E) + (4 * qi + c < w.P0 ? 0 : w.W);
+            atomicAdd(&w.part[bin], 1);
+        }
+    }
+}
+
+// Own entries: rank among the same wave's lower lanes, and per-wave counts
+// (the lowest lane of each expert's peers records them).  Returns the rank
+// among lower lanes.
+__device__ __forceinline__ int32_t rank_own(const Part& w, int rw, int32_t own_id) {
+    int32_t below = 0;
+    if (w.wave < rw) {
+        const bool mine = valid_id(own_id, w.E);
+        const uint64_t peers = match_peers(static_cast<uint32_t>(own_id), key_bits(w.E), __ballot(mine));
+        const uint64_t lower = peers & lanemask_lt();
+        below = __popcll(lower);
+        if (mine && lower == 0) w.wcnt[w.wave * w.W + own_id] = __popcll(peers);
+    }
+    return below;
+}
+
+// After the histograms and the own ranks are complete (barrier before):
+// offsets (exclusive scan of the totals over experts), the entries the
+// capacity drops, the own entries' slots (to LDS, and to slot_of /
+// src_of_slot from the workgroup holding the token's chunk 0), count,
+// offset and status (workgroup 0), and the receive rows no entry fills.
+// Ends with a barrier.
+__device__ __forceinline__ void finish_layout(const PersistParams& p, const Part& w,
+                                              int32_t own_id, int32_t below, int32_t* s_wsum,
+                                              int32_t* s_wover) {
+    const int tid = w.tid, E = w.E, W = w.W;
+    int32_t tot = 0, over = 0;
+    if (tid < E) {
+        tot = w.part[tid] + w.part[W + tid];
+        over = (p.cap > 0 && tot > p.cap) ? tot - p.cap : 0;
+    }
+    const int32_t incl = wave_inclusive_scan(tot);
+    const int32_t oincl = wave_inclusive_scan(over);
+    if (w.lane == kWave - 1) {
+        s_wsum[w.wave] = incl;
+        s_wover[w.wave] = oincl;
+    }
+    __syncthreads();
+    int32_t before = 0;
+    for (int v = 0; v < w.wave; ++v) before += s_wsum[v];
+    if (tid < E) {
+        w.off[tid] = before + incl - tot;
+        if (w.b == 0) {
+            p.count[tid] = tot;
+            p.offset[tid] = before + incl - tot;
+        }
+    }
+    if (tid == 0) {
+        int32_t valid = 0, drop = 0;
+        for (int v = 0; v < kWaves; ++v) {
+            valid += s_wsum[v];
+            drop += s_wover[v];
+        }
+        w.off[E] = valid;
+        if (w.b == 0) {
+            p.offset[E] = valid;
+            p.status[0] = w.part[E] + w.part[W + E];
+            p.status[1] = drop;
+        }
+    }
+    __syncthreads();
+
+    if (tid < w.n_own) {
+        int32_t slot = -1;
+        if (valid_id(own_id, E)) {
+            int32_t r = w.part[own_id] + below;
+            for (int v = 0; v < w.wave; ++v) r += w.wcnt[v * W + own_id];
+            if (p.cap == 0) slot = w.off[own_id] + r;
+            else if (r < p.cap) slot = own_id * p.cap + r;
+        }
+        w.s_slot[(tid / w.k) * w.kp + tid % w.k] = slot;
+        // the workgroup holding the token's chunk 0 writes its layout entries
+        const int t = w.tA + tid / w.k;
+        if (t * p.C >= w.c_begin) {
+            p.slot_of[w.P0 + tid] = slot;
+            if (slot >= 0 && slot < p.R) p.src_of_slot[slot] = w.P0 + tid;
+        }
+    }
+    // Receive rows no entry fills: past each expert's count (fixed capacity,
+    // experts b, b + nwg, ...), or past the valid entries (contiguous).
+    if (p.cap > 0) {
+        for (int e = w.b; e < E; e += p.nwg) {
+            int32_t* rows = p.src_of_slot + static_cast<int64_t>(e) * p.cap;
+            const int32_t filled = min(w.part[e] + w.part[W + e], p.cap);
+            for (int r = filled + tid; r < p.cap; r += kThreads) rows[r] = -1;
+        }
+    } else {
+        for (int64_t r = w.off[E] + static_cast<int64_t>(w.b) * kThreads + tid; r < p.R;
+             r += static_cast<int64_t>(p.nwg) * kThreads)
+            p.src_of_slot[r] = -1;
+    }
+    __syncthreads();
+}
+
+// Issue priority for chunk j of Q: it falls from 3 to 0 over the quarters of
+// a wave's chunks, so that a SIMD issues for its oldest wave first and a wave
+// ahead of the others yields the SIMD to them, as in the persistent combine.
+__device__ __forceinline__ void lower_priority(int j, int Q) {
+    const int level = (4 * (j + 1)) / Q;
+    if (level == 1) __builtin_amdgcn_s_setprio(2);
+    else if (level == 2) __builtin_amdgcn_s_setprio(1);
+    else if (level >= 3) __builtin_amdgcn_s_setprio(0);
+}
+
+// The k slots of the token a chunk belongs to, the same in every lane.
+template <int K>
+struct TokenSlots {
+    int32_t s[K > 0 ? K : 1];
+    __device__ __forceinline__ void read(const int32_t* sl) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) s[j] = __builtin_amdgcn_readfirstlane(sl[j]);
+    }
+};
+
 // K: the top-k count when it is 1..8 (the store loop is unrolled over the
 // token's receive rows, read from LDS together), 0 for any k.
 template <int K>
@@ -116,33 +291,14 @@ void layout_dispatch_persistent_kernel(PersistParams p) {
     __shared__ int32_t s_wsum[kWaves];
     __shared__ int32_t s_wover[kWaves];
 
-    const int tid = static_cast<int>(threadIdx.x);
-    const int lane = static_cast<int>(lane_id());
-    // the same for every lane of a wave: scalar from here on
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int b = static_cast<int>(blockIdx.x);
-    const int E = p.E;
-    const int k = K > 0 ? K : p.k;
-    const int kp = slot_stride(k);
-    const int W = E + 1;
-    int32_t* part = s_dyn;
-    int32_t* off = part + 2 * W;
-    int32_t* wcnt = off + W;
-    int32_t* s_slot = s_dyn + ((static_cast<size_t>(3 + p.rw) * W + 3) & ~static_cast<size_t>(3));
-
-    const int all_chunks = p.T * p.C;  // < 2^31: at most (CUs * 16 * kHold) here
-    const int c_begin = b * kWaves * p.Q;
-    const int c_end = min(c_begin + kWaves * p.Q, all_chunks);
-    const bool has = c_begin < c_end;
-    const int tA = has ? c_begin / p.C : 0;
-    const int tB = has ? (c_end - 1) / p.C + 1 : 0;
-    const int P0 = tA * k;         // the workgroup's first routing entry
-    const int n_own = (tB - tA) * k;  // <= rw * 64 (host-checked)
+    const Part w = make_part<K>(p, s_dyn);
+    const int tid = w.tid, lane = w.lane, wave = w.wave;
+    const int k = w.k;
 
     // 1. Loads, in the order their results are needed: a wave's loads return
     // in issue order.  The own entry (clamped address: unconditional) ...
-    const int32_t own_raw = p.idx[P0 + min(tid, max(n_own, 1) - 1)];
-    const int32_t own_id = (tid < n_own) ? own_raw : -1;
+    const int32_t own_raw = p.idx[w.P0 + min(tid, max(w.n_own, 1) - 1)];
+    const int32_t own_id = (tid < w.n_own) ? own_raw : -1;
     // ... the routing table (n is a multiple of 4; quads past the end load
     // the last quad again and are not counted) ...
     const int4* quads = reinterpret_cast<const int4*>(p.idx);
@@ -157,13 +313,13 @@ void layout_dispatch_persistent_kernel(PersistParams p) {
     // because with loads under branches the compiler could no longer count
     // which of them are still in flight, and the histogram below would wait
     // for the rows instead of only for the table.
-    const int c_last = max(c_end - 1, 0);
+    const int c_last = max(w.c_end - 1, 0);
     u32x4 buf[kHold];
     int cid[kHold];
 #pragma unroll
     for (int j = 0; j < kHold; ++j) {
-        const int c = c_begin + wave + j * kWaves;
-        const bool mine = j < p.Q && c < c_end;
+        const int c = w.c_begin + wave + j * kWaves;
+        const bool mine = j < p.Q && c < w.c_end;
         const int cc = mine ? c : c_last;
         const int t = cc / p.C;
         const int v = min((cc - t * p.C) * kWave + lane, p.nvec - 1);
@@ -171,121 +327,35 @@ void layout_dispatch_persistent_kernel(PersistParams p) {
         cid[j] = mine ? c : -1;
     }
 
-    for (int e = tid; e < (2 + p.rw) * W; e += kThreads)
-        (e < 2 * W ? part[e] : wcnt[e - 2 * W]) = 0;
+    for (int e = tid; e < (2 + p.rw) * w.W; e += kThreads)
+        (e < 2 * w.W ? w.part[e] : w.wcnt[e - 2 * w.W]) = 0;
     __syncthreads();
 
-    // 2. Histograms of the table, split at the workgroup's first entry.
-    auto count_quad = [&](const int4& g, int qi) {
-        if (qi < nq) {
-            const int32_t id4[4] = {g.x, g.y, g.z, g.w};
+    // 2. Histograms of the table, split at the workgroup's first entry, and
+    // the own entries' ranks.
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int32_t id = id4[c];
-                const int bin = (valid_id(id, E) ? id : E) + (4 * qi + c < P0 ? 0 : W);
-                atomicAdd(&part[bin], 1);
-            }
-        }
-    };
-#pragma unroll
-    for (int u = 0; u < kIdQuads; ++u) count_quad(q[u], u * kThreads + tid);
-
-    // Own entries: rank among the same wave's lower lanes, and per-wave
-    // counts (the lowest lane of each expert's peers records them).
-    int32_t below = 0;
-    if (wave < p.rw) {
-        const bool mine = valid_id(own_id, E);
-        const uint64_t peers = match_peers(static_cast<uint32_t>(own_id), key_bits(E), __ballot(mine));
-        const uint64_t lower = peers & lanemask_lt();
-        below = __popcll(lower);
-        if (mine && lower == 0) wcnt[wave * W + own_id] = __popcll(peers);
-    }
+    for (int u = 0; u < kIdQuads; ++u) count_quad(w, nq, q[u], u * kThreads + tid);
+    const int32_t below = rank_own(w, p.rw, own_id);
     __syncthreads();
 
-    // 3. Offsets (exclusive scan of the totals over experts), the entries the
-    // capacity drops, then the own entries' slots.
-    int32_t tot = 0, over = 0;
-    if (tid < E) {
-        tot = part[tid] + part[W + tid];
-        over = (p.cap > 0 && tot > p.cap) ? tot - p.cap : 0;
-    }
-    const int32_t incl = wave_inclusive_scan(tot);
-    const int32_t oincl = wave_inclusive_scan(over);
-    if (lane == kWave - 1) {
-        s_wsum[wave] = incl;
-        s_wover[wave] = oincl;
-    }
-    __syncthreads();
-    int32_t before = 0;
-    for (int w = 0; w < wave; ++w) before += s_wsum[w];
-    if (tid < E) {
-        off[tid] = before + incl - tot;
-        if (b == 0) {
-            p.count[tid] = tot;
-            p.offset[tid] = before + incl - tot;
-        }
-    }
-    if (tid == 0) {
-        int32_t valid = 0, drop = 0;
-        for (int w = 0; w < kWaves; ++w) {
-            valid += s_wsum[w];
-            drop += s_wover[w];
-        }
-        off[E] = valid;
-        if (b == 0) {
-            p.offset[E] = valid;
-            p.status[0] = part[E] + part[W + E];
-            p.status[1] = drop;
-        }
-    }
-    __syncthreads();
-
-    if (tid < n_own) {
-        int32_t slot = -1;
-        if (valid_id(own_id, E)) {
-            int32_t r = part[own_id] + below;
-            for (int w = 0; w < wave; ++w) r += wcnt[w * W + own_id];
-            if (p.cap == 0) slot = off[own_id] + r;
-            else if (r < p.cap) slot = own_id * p.cap + r;
-        }
-        s_slot[(tid / k) * kp + tid % k] = slot;
-        // the workgroup holding the token's chunk 0 writes its layout entries
-        const int t = tA + tid / k;
-        if (t * p.C >= c_begin) {
-            p.slot_of[P0 + tid] = slot;
-            if (slot >= 0 && slot < p.R) p.src_of_slot[slot] = P0 + tid;
-        }
-    }
-    // Receive rows no entry fills: past each expert's count (fixed capacity,
-    // experts b, b + nwg, ...), or past the valid entries (contiguous).
-    if (p.cap > 0) {
-        for (int e = b; e < E; e += p.nwg) {
-            int32_t* rows = p.src_of_slot + static_cast<int64_t>(e) * p.cap;
-            const int32_t filled = min(part[e] + part[W + e], p.cap);
-            for (int r = filled + tid; r < p.cap; r += kThreads) rows[r] = -1;
-        }
-    } else {
-        for (int64_t r = off[E] + static_cast<int64_t>(b) * kThreads + tid; r < p.R;
-             r += static_cast<int64_t>(p.nwg) * kThreads)
-            p.src_of_slot[r] = -1;
-    }
-    __syncthreads();
+    // 3. Offsets, slots and the layout outputs.
+    finish_layout(p, w, own_id, below, s_wsum, s_wover);
 
     // 4. Stores: one wait for the rows, then every store of the wave with no
     // wait in between.
+    u32x4* recv = static_cast<u32x4*>(p.recv_x);
     auto store_chunk = [&](int c, const u32x4& data) {
         const int t = c / p.C;
         const int v = min((c - t * p.C) * kWave + lane, p.nvec - 1);
-        const int32_t* sl = s_slot + (t - tA) * kp;
-        u32x4* dst = p.recv_x + v;
+        const int32_t* sl = w.s_slot + (t - w.tA) * w.kp;
+        u32x4* dst = recv + v;
         if (K > 0) {
-            int32_t slot[K > 0 ? K : 1];
-#pragma unroll
-            for (int j = 0; j < K; ++j) slot[j] = __builtin_amdgcn_readfirstlane(sl[j]);
+            TokenSlots<K> ts;
+            ts.read(sl);
 #pragma unroll
             for (int j = 0; j < K; ++j)
-                if (slot[j] >= 0 && slot[j] < p.R)
-                    __builtin_nontemporal_store(data, dst + static_cast<int64_t>(slot[j]) * p.nvec);
+                if (ts.s[j] >= 0 && ts.s[j] < p.R)
+                    __builtin_nontemporal_store(data, dst + static_cast<int64_t>(ts.s[j]) * p.nvec);
         } else {
             for (int j = 0; j < k; ++j) {
                 const int32_t slot = __builtin_amdgcn_readfirstlane(sl[j]);
@@ -295,35 +365,198 @@ void layout_dispatch_persistent_kernel(PersistParams p) {
         }
     };
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    // Issue priority falls from 3 to 0 over the quarters of a wave's chunks:
-    // a SIMD issues for its oldest wave first, and a wave ahead of the others
-    // yields the SIMD to them, as in the persistent combine.
     __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int j = 0; j < kHold; ++j) {
         if (cid[j] >= 0) {  // uniform
             store_chunk(cid[j], buf[j]);
-            const int level = (4 * (j + 1)) / p.Q;
-            if (level == 1) __builtin_amdgcn_s_setprio(2);
-            else if (level == 2) __builtin_amdgcn_s_setprio(1);
-            else if (level >= 3) __builtin_amdgcn_s_setprio(0);
+            lower_priority(j, p.Q);
         }
     }
 }
 
+// FP8 rows.  The same layout; each chunk is quantised (one 128-channel block
+// per 16 lanes, as in the other dispatch kernels) and stored as soon as it
+// has arrived and the layout is known.  A wave's loads are all issued before
+// its first store, and the wait for a load does not wait for stores issued
+// after it, so quantising chunk j waits only for chunk j.
+//
+// UE8M0: power-of-two scales held as exponent bytes.
+template <int K, bool UE8M0>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void layout_dispatch_persistent_fp8_kernel(PersistParams p) {
+    extern __shared__ __align__(16) int32_t s_dyn[];
+    __shared__ int32_t s_wsum[kWaves];
+    __shared__ int32_t s_wover[kWaves];
+
+    const Part w = make_part<K>(p, s_dyn);
+    const int tid = w.tid, lane = w.lane, wave = w.wave;
+    const int k = w.k;
+
+    // Loads as in the bf16 kernel: the own entry, the table, the rows.
+    const int32_t own_raw = p.idx[w.P0 + min(tid, max(w.n_own, 1) - 1)];
+    const int32_t own_id = (tid < w.n_own) ? own_raw : -1;
+    const int4* quads = reinterpret_cast<const int4*>(p.idx);
+    const int nq = p.n / 4;
+    int4 q[kIdQuads];
+#pragma unroll
+    for (int u = 0; u < kIdQuads; ++u) q[u] = quads[min(u * kThreads + tid, nq - 1)];
+    // Chunk j of the wave: pieces past the end of the row map, 16 lanes at a
+    // time, onto the row's last 128-channel block (they redo its codes and
+    // store the same bytes to the same place).
+    const int c_last = max(w.c_end - 1, 0);
+    u32x4 buf[kHoldFp8];
+    int cid[kHoldFp8];
+#pragma unroll
+    for (int j = 0; j < kHoldFp8; ++j) {
+        const int c = w.c_begin + wave + j * kWaves;
+        const bool mine = j < p.Q && c < w.c_end;
+        const int cc = mine ? c : c_last;
+        const int t = cc / p.C;
+        const int vv = (cc - t * p.C) * kWave + lane;
+        const int v = vv < p.nvec ? vv : p.nvec - 16 + (vv & 15);
+        buf[j] = __builtin_nontemporal_load(p.x + static_cast<int64_t>(t) * p.nvec + v);
+        cid[j] = mine ? c : -1;
+    }
+
+    for (int e = tid; e < (2 + p.rw) * w.W; e += kThreads)
+        (e < 2 * w.W ? w.part[e] : w.wcnt[e - 2 * w.W]) = 0;
+    __syncthreads();
+
+#pragma unroll
+    for (int u = 0; u < kIdQuads; ++u) count_quad(w, nq, q[u], u * kThreads + tid);
+    const int32_t below = rank_own(w, p.rw, own_id);
+    __syncthreads();
+
+    finish_layout(p, w, own_id, below, s_wsum, s_wover);
+
+    u32x2* recv = static_cast<u32x2*>(p.recv_x);
+    auto quant_store = [&](int c, const u32x4& data) {
+        const int t = c / p.C;
+        const int vv = (c - t * p.C) * kWave + lane;
+        const int v = vv < p.nvec ? vv : p.nvec - 16 + (vv & 15);
+        const float amax = dispatch::row16_max(dispatch::absmax8(data));
+        u32x2 code;
+        float sval;  // fp32 scale, or the UE8M0 exponent byte
+        if (UE8M0) {
+            const int s = dispatch::ue8m0_exponent(amax);
+            const float factor = __uint_as_float(static_cast<uint32_t>(127 - s) << 23);
+            code = dispatch::quant8_pow2(data, factor, amax == 0.0f);
+            sval = static_cast<float>(s + 127);
+        } else {
+            const float scale = amax / 448.0f;
+            code = dispatch::quant8(data, scale);
+            sval = scale;
+        }
+        const int32_t* sl = w.s_slot + (t - w.tA) * w.kp;
+        u32x2* dst = recv + v;
+        // one lane per block writes its scale (plain stores: the 16-byte
+        // pieces of a scale row from the row's chunks meet in L2)
+        const bool scale_lane = (lane & 15) == 0 && vv < p.nvec;
+        const int64_t sidx = vv >> 4;
+        if (K > 0) {
+            TokenSlots<K> ts;
+            ts.read(sl);
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                if (ts.s[j] >= 0 && ts.s[j] < p.R)
+                    __builtin_nontemporal_store(code, dst + static_cast<int64_t>(ts.s[j]) * p.nvec);
+            if (scale_lane) {
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    if (ts.s[j] < 0 || ts.s[j] >= p.R) continue;
+                    const int64_t at = static_cast<int64_t>(ts.s[j]) * p.nblk + sidx;
+                    if (UE8M0) static_cast<uint8_t*>(p.recv_scales)[at] = static_cast<uint8_t>(sval);
+                    else static_cast<float*>(p.recv_scales)[at] = sval;
+                }
+            }
+        } else {
+            for (int j = 0; j < k; ++j) {
+                const int32_t slot = __builtin_amdgcn_readfirstlane(sl[j]);
+                if (slot < 0 || slot >= p.R) continue;
+                __builtin_nontemporal_store(code, dst + static_cast<int64_t>(slot) * p.nvec);
+                if (scale_lane) {
+                    const int64_t at = static_cast<int64_t>(slot) * p.nblk + sidx;
+                    if (UE8M0) static_cast<uint8_t*>(p.recv_scales)[at] = static_cast<uint8_t>(sval);
+                    else static_cast<float*>(p.recv_scales)[at] = sval;
+                }
+            }
+        }
+    };
+    __builtin_amdgcn_s_setprio(3);
+#pragma unroll
+    for (int j = 0; j < kHoldFp8; ++j) {
+        if (cid[j] >= 0) {  // uniform
+            quant_store(cid[j], buf[j]);
+            lower_priority(j, p.Q);
+        }
+    }
+}
+
+struct PersistShape {
+    int C, Q, maxtok, rw;
+};
+
+PersistShape persist_shape(const ep_problem& p, int ncu) {
+    PersistShape s;
+    const int nvec = p.hidden / 8;
+    s.C = (nvec + kWave - 1) / kWave;
+    const int64_t nw = static_cast<int64_t>(ncu) * kWaves;
+    s.Q = static_cast<int>((static_cast<int64_t>(p.num_tokens) * s.C + nw - 1) / nw);
+    s.maxtok = (kWaves * s.Q - 1) / s.C + 2;
+    s.rw = (s.maxtok * p.num_topk + kWave - 1) / kWave;
+    return s;
+}
+
+template <template <int> class Launch, typename... A>
+void launch_by_k(int k, A... a) {
+    switch (k) {
+        case 1: Launch<1>::run(a...); break;
+        case 2: Launch<2>::run(a...); break;
+        case 3: Launch<3>::run(a...); break;
+        case 4: Launch<4>::run(a...); break;
+        case 5: Launch<5>::run(a...); break;
+        case 6: Launch<6>::run(a...); break;
+        case 7: Launch<7>::run(a...); break;
+        case 8: Launch<8>::run(a...); break;
+        default: Launch<0>::run(a...); break;
+    }
+}
+
+template <int K>
+struct LaunchBf16 {
+    static void run(const PersistParams& a, dim3 grid, size_t lds, hipStream_t stream) {
+        hipLaunchKernelGGL(layout_dispatch_persistent_kernel<K>, grid, dim3(kThreads), lds, stream, a);
+    }
+};
+template <int K>
+struct LaunchFp8 {
+    static void run(const PersistParams& a, dim3 grid, size_t lds, hipStream_t stream) {
+        hipLaunchKernelGGL((layout_dispatch_persistent_fp8_kernel<K, false>), grid, dim3(kThreads), lds, stream, a);
+    }
+};
+template <int K>
+struct LaunchUe8m0 {
+    static void run(const PersistParams& a, dim3 grid, size_t lds, hipStream_t stream) {
+        hipLaunchKernelGGL((layout_dispatch_persistent_fp8_kernel<K, true>), grid, dim3(kThreads), lds, stream, a);
+    }
+};
+
 }  // namespace
 
 bool layout_dispatch_persistent_fits(const ep_problem& p, int ncu) {
-    if (p.use_fp8 != 0 || p.num_tokens <= 0) return false;
+    if (p.num_tokens <= 0) return false;
+    const bool fp8 = p.use_fp8 != 0;
     const int64_t n = static_cast<int64_t>(p.num_tokens) * p.num_topk;
     // whole quads of routing entries (the table is loaded 16 bytes a lane)
     if (n <= kFusedMaxEntries || n > kMaxIds || n % 4 != 0) return false;
+    if (fp8 && p.hidden % 128 != 0) return false;
     const int nvec = p.hidden / 8;
     const int64_t C = (nvec + kWave - 1) / kWave;
     const int64_t nw = static_cast<int64_t>(ncu) * kWaves;
     const int64_t all_chunks = static_cast<int64_t>(p.num_tokens) * C;
     // every wave gets a chunk, and one launch holds all of them
-    if (all_chunks < nw || all_chunks > nw * kHold) return false;
+    if (all_chunks < nw || all_chunks > nw * (fp8 ? kHoldFp8 : kHold)) return false;
     const int64_t Q = (all_chunks + nw - 1) / nw;
     const int64_t maxtok = (kWaves * Q - 1) / C + 2;
     const int64_t own = maxtok * p.num_topk;
@@ -334,7 +567,7 @@ bool layout_dispatch_persistent_fits(const ep_problem& p, int ncu) {
 
 hipError_t launch_layout_dispatch_persistent(const ep_problem& p, const int32_t* topk_idx,
                                              const ep_layout_t& out, const void* x, void* recv_x,
-                                             int ncu, hipStream_t stream) {
+                                             void* recv_scales, int ncu, hipStream_t stream) {
     PersistParams a;
     a.idx = topk_idx;
     a.n = p.num_tokens * p.num_topk;
@@ -348,28 +581,22 @@ hipError_t launch_layout_dispatch_persistent(const ep_problem& p, const int32_t*
     a.src_of_slot = out.src_of_slot;
     a.status = out.status;
     a.x = static_cast<const u32x4*>(x);
-    a.recv_x = static_cast<u32x4*>(recv_x);
+    a.recv_x = recv_x;
+    a.recv_scales = recv_scales;
     a.T = p.num_tokens;
     a.nvec = p.hidden / 8;
-    a.C = (a.nvec + kWave - 1) / kWave;
-    const int64_t nw = static_cast<int64_t>(ncu) * kWaves;
-    a.Q = static_cast<int>((static_cast<int64_t>(a.T) * a.C + nw - 1) / nw);
-    a.maxtok = (kWaves * a.Q - 1) / a.C + 2;
-    a.rw = (a.maxtok * a.k + kWave - 1) / kWave;
+    a.nblk = p.hidden / 128;
+    const PersistShape s = persist_shape(p, ncu);
+    a.C = s.C;
+    a.Q = s.Q;
+    a.maxtok = s.maxtok;
+    a.rw = s.rw;
     a.nwg = ncu;
     const size_t lds = persist_lds_words(a.E, a.rw, a.maxtok, a.k) * 4;
-    const dim3 grid(ncu), block(kThreads);
-    switch (a.k) {
-        case 1: hipLaunchKernelGGL(layout_dispatch_persistent_kernel<1>, grid, block, lds, stream, a); break;
-        case 2: hipLaunchKernelGGL(layout_dispatch_persistent_kernel<2>, grid, block, lds, stream, a); break;
-        case 3: hipLaunchKernelGGL(layout_dispatch_persistent_kernel<3>, grid, block, lds, stream, a); break;
-        case 4: hipLaunchKernelGGL(layout_dispatch_persistent_kernel<4>, grid, block, lds, stream, a); break;
-        case 5: hipLaunchKernelGGL(layout_dispatch_persistent_kernel<5>, grid, block, lds, stream, a); break;
-        case 6: hipLaunchKernelGGL(layout_dispatch_persistent_kernel<6>, grid, block, lds, stream, a); break;
-        case 7: hipLaunchKernelGGL(layout_dispatch_persistent_kernel<7>, grid, block, lds, stream, a); break;
-        case 8: hipLaunchKernelGGL(layout_dispatch_persistent_kernel<8>, grid, block, lds, stream, a); break;
-        default: hipLaunchKernelGGL(layout_dispatch_persistent_kernel<0>, grid, block, lds, stream, a); break;
-    }
+    const dim3 grid(ncu);
+    if (p.use_fp8 == 0) launch_by_k<LaunchBf16>(a.k, a, grid, lds, stream);
+    else if (p.use_fp8 == 1) launch_by_k<LaunchFp8>(a.k, a, grid, lds, stream);
+    else launch_by_k<LaunchUe8m0>(a.k, a, grid, lds, stream);
     return hipGetLastError();
 }
 

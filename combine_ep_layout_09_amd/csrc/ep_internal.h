@@ -69,13 +69,13 @@ hipError_t launch_dispatch(const ep_problem& p, const void* x, const int32_t* sl
 hipError_t launch_layout_dispatch(const ep_problem& p, const int32_t* topk_idx,
                                   const ep_layout_t& out, void* workspace, const void* x,
                                   void* recv_x, void* recv_scales, hipStream_t stream);
-// Prefill-sized tables with bf16 payloads: layout and dispatch in one launch
-// of one workgroup per CU (ncu CUs), each holding its share of the rows in
-// registers.  fits() says whether the problem takes that form.
+// Prefill-sized tables: layout and dispatch in one launch of one workgroup
+// per CU (ncu CUs), each holding its share of the rows in registers.  fits()
+// says whether the problem takes that form.
 bool layout_dispatch_persistent_fits(const ep_problem& p, int ncu);
 hipError_t launch_layout_dispatch_persistent(const ep_problem& p, const int32_t* topk_idx,
                                              const ep_layout_t& out, const void* x, void* recv_x,
-                                             int ncu, hipStream_t stream);
+                                             void* recv_scales, int ncu, hipStream_t stream);
 hipError_t launch_combine(const ep_problem& p, const void* expert_out, const int32_t* slot_of,
                           const float* topk_weights, void* y, hipStream_t stream);
 hipError_t launch_e4m3_encode(const float* in, uint8_t* out, int64_t n, hipStream_t stream);

@@ -163,12 +163,13 @@ int ep_dispatch(const ep_problem* prob, const void* x, const ep_layout_t* layout
  * (T*k, decode-sized batches) it is one kernel launch in which no workgroup
  * waits for another: each one derives the slots of its own tokens from the
  * whole table while its rows load, then stores them; the workspace is not
- * touched.  Prefill-sized tables with bf16 payloads (8192 < T*k <= 32768,
- * T*k a multiple of 4, token rows that give every wave of one 1024-lane
- * workgroup per CU between 1 and 14 chunks of 1 KiB) are one launch too:
- * each workgroup histograms the whole table itself while its share of the
- * rows loads, ranks its own tokens' entries, then stores; the workspace is
- * not touched.  Other tables take two launches for bf16 payloads and for FP8
+ * touched.  Prefill-sized tables (8192 < T*k <= 32768, T*k a multiple of
+ * 4, token rows that give every wave of one 1024-lane workgroup per CU
+ * between 1 and 14 (bf16) or 16 (FP8) chunks of 64 16-byte pieces) are one
+ * launch too: each workgroup histograms the whole table itself while its
+ * share of the rows loads, ranks its own tokens' entries, then stores (FP8:
+ * quantises and stores each chunk as it arrives); the workspace is not
+ * touched.  Other tables take two launches for bf16 payloads and for FP8
  * with k >= 8: the layout's histogram kernel (which also writes per-block
  * prefix sums over experts to the workspace), then a dispatch kernel in
  * which each workgroup computes its own token's slots from those tables and

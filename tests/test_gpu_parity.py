@@ -251,12 +251,25 @@ EDGE = [
     dict(T=1700, H=2048, k=8, E=1024, cap=0, fp8=False, name="persistent_dispatch_max_experts"),
     dict(T=1024, H=4096, k=32, E=128, cap=0, fp8=False, name="persistent_dispatch_k32_largest_table"),
     dict(T=12000, H=512, k=2, E=1, cap=0, fp8=False, name="persistent_dispatch_one_expert"),
-    # FP8 rows at prefill sizes (the multi-kernel forms): rows of 15 blocks
-    # (two 7-block tiles and a ragged one), UE8M0 scales with capacity
-    # overflow, 49152 entries over 48 experts
+    # FP8 rows at prefill sizes (8192 < T*k <= 49152 with at least one
+    # 64-piece chunk per wave: the one-launch form; else the multi-kernel
+    # forms): rows of 15 blocks (a last chunk of 3 blocks), UE8M0 scales with
+    # capacity overflow, 49152 entries over 48 experts
     dict(T=2000, H=1920, k=8, E=64, cap=0, fp8=1, name="prefill_fp8_ragged_blocks"),
     dict(T=3000, H=1024, k=6, E=32, cap=400, fp8=2, name="prefill_ue8m0_capacity_overflow"),
     dict(T=8192, H=4096, k=6, E=48, cap=0, fp8=1, name="prefill_fp8_k6_48_experts"),
+    # the one-launch FP8 form: tokens straddling two workgroups, an odd k with
+    # a last chunk of 2 blocks, k above 8 (the generic store loop) with UE8M0
+    # scales, k = 32, the most experts with capacity overflow, a table that
+    # fills the second half of the table registers only in part, a row of
+    # one block
+    dict(T=1500, H=2560, k=8, E=64, cap=0, fp8=1, name="persistent_fp8_straddle"),
+    dict(T=2400, H=1792, k=5, E=37, cap=0, fp8=1, name="persistent_fp8_odd_k_ragged_chunk"),
+    dict(T=1300, H=3072, k=12, E=256, cap=0, fp8=2, name="persistent_ue8m0_k12"),
+    dict(T=1024, H=4096, k=32, E=128, cap=0, fp8=1, name="persistent_fp8_k32"),
+    dict(T=1700, H=2048, k=8, E=1024, cap=12, fp8=2, name="persistent_ue8m0_max_experts_capacity"),
+    dict(T=5000, H=1024, k=8, E=160, cap=0, fp8=1, name="persistent_fp8_table_second_half_partial"),
+    dict(T=12000, H=2816, k=1, E=3, cap=0, fp8=1, name="persistent_fp8_k1_22_blocks"),
     # the persistent combine at 14 chunks per wave: a partly filled last
     # workgroup with ragged rows (875 pieces per row: 13 full chunks and one
     # of 43), and k = 1 with capacity drops (entries without a slot)
@@ -430,6 +443,19 @@ def test_fp8_special_rows():
                  name=f"fp8_special_cap{cap}")
         c.nan_unused_rows()
         check_case(c, run_gpu(c))
+        check_case(c, run_gpu(c, fused=True))
+
+
+def test_fp8_special_rows_prefill():
+    """The same special rows at a prefill size (2100 tokens, k = 8: the
+    one-launch layout + dispatch of FP8 rows), with fp32 and UE8M0 scales,
+    with and without capacity."""
+    rng = np.random.default_rng(32)
+    T, H, E, k = 2100, 1024, 40, 8
+    x = workloads.to_bf16_bits(_fp8_special_xf(rng, T, H))
+    for mode, cap in ((1, 0), (2, 0), (1, 500), (2, 500)):
+        c = _random_case(T, H, k, E, cap, mode, seed=mode + cap, name=f"fp8_special_prefill_m{mode}_cap{cap}")
+        c.x = x
         check_case(c, run_gpu(c, fused=True))
 
 

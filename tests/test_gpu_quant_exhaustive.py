@@ -158,13 +158,14 @@ def test_dispatch_quantiser_every_pair():
 def test_layout_dispatch_quantiser_sampled_ranges(mode):
     """The same inputs through ep_layout_dispatch, whose other forms carry
     their own copy of the tile code: the one-kernel form for small tables
-    (512 tokens, k = 8: 4096 routing entries) and the ranking dispatch kernel
-    (k = 8 above 8192 entries), on the first, a middle and the last range of
-    block maxima."""
+    (512 tokens, k = 8: 4096 routing entries), the one-launch form of one
+    workgroup per CU (4096 tokens: 32768 entries) and the ranking dispatch
+    kernel (8192 tokens: 65536 entries), on the first, a middle and the last
+    range of block maxima."""
     picks = [AMAX_RANGES[0], AMAX_RANGES[len(AMAX_RANGES) // 2], AMAX_RANGES[-1]]
     for a0, a1 in picks:
         rows = exhaustive_rows(a0, a1)
-        for T in (512, 8192):
+        for T in (512, 4096, 8192):
             for start in range(0, rows.shape[0], max(T, rows.shape[0] // 3)):
                 x_host = np.ascontiguousarray(rows[start:start + T])
                 print(f"[gpu] layout_dispatch quantiser mode {mode}: maxima "
