@@ -221,16 +221,17 @@ def one_launch(wl):
 
 def persistent_launch(wl, ncu):
     """Whether ep_layout_dispatch takes its one-launch form of one 1024-lane
-    workgroup per CU (the library's rule: bf16 rows, 8192 < T*k <= 32768,
-    T*k a multiple of 4, between 1 and 14 chunks of 64 pieces per wave, the
-    workgroup's own entries within 1024 and its LDS within 64 KiB)."""
+    workgroup per CU (the library's rule: 8192 < T*k <= 32768, T*k a
+    multiple of 4, between 1 and 14 (bf16) or 16 (FP8) chunks of 64 pieces
+    per wave, the workgroup's own entries within 1024 and its LDS within
+    64 KiB)."""
     n = wl.T * wl.k
-    if wl.fp8 or n <= 8192 or n > 32768 or n % 4:
+    if n <= 8192 or n > 32768 or n % 4 or (wl.fp8 and wl.H % 128):
         return False
     C = -(-(wl.H // 8) // 64)
     nw = ncu * 16
     chunks = wl.T * C
-    if chunks < nw or chunks > nw * 14:
+    if chunks < nw or chunks > nw * (16 if wl.fp8 else 14):
         return False
     Q = -(-chunks // nw)
     maxtok = (16 * Q - 1) // C + 2
@@ -247,6 +248,7 @@ def persistent_launch(wl, ncu):
 FUSED_SOURCES = {
     "layout_dispatch_small_kernel": ("ep_fused.hip",),
     "layout_dispatch_persistent_kernel": ("ep_fused_persist.hip",),
+    "layout_dispatch_persistent_fp8_kernel": ("ep_fused_persist.hip",),
     "layout_hist_kernel+layout_dispatch_ranked_kernel": ("ep_fused.hip", "ep_layout.hip"),
     "layout_hist_kernel+layout_rank_kernel+dispatch_fp8_kernel": ("ep_layout.hip", "ep_dispatch.hip"),
     "layout_whole_kernel+dispatch_fp8_kernel": ("ep_layout.hip", "ep_dispatch.hip"),
@@ -256,13 +258,13 @@ FUSED_SOURCES = {
 def fused_call_name(wl, ncu):
     """The kernels of one ep_layout_dispatch call on this workload (the
     library's rule: one kernel for small tables; one persistent kernel for
-    prefill-sized bf16 tables that fit it; the histogram kernel and the
+    prefill-sized tables that fit it; the histogram kernel and the
     ranking dispatch kernel for other bf16 rows or k >= 8; otherwise the
     layout kernel(s) and the dispatch kernel)."""
     if one_launch(wl):
         return "layout_dispatch_small_kernel"
     if persistent_launch(wl, ncu):
-        return "layout_dispatch_persistent_kernel"
+        return "layout_dispatch_persistent_fp8_kernel" if wl.fp8 else "layout_dispatch_persistent_kernel"
     if not wl.fp8 or wl.k >= 8:
         return "layout_hist_kernel+layout_dispatch_ranked_kernel"
     if whole_table_layout(wl):
