@@ -274,10 +274,12 @@ def fused_call_name(wl, ncu):
 
 def whole_table_layout(wl):
     """Whether ep_layout takes its one-kernel form for mid-size tables (the
-    library's rule: 8192 < T*k <= 65536, at least 128 experts, and
-    19 (E + 1) int32 of LDS within 64 KiB)."""
+    library's rule: 8192 < T*k <= 65536, at least 32 experts, and its LDS --
+    (2 c + 17) (E + 1) int32 with c = 8 histogram copies below 128 experts,
+    else 1 -- within 64 KiB)."""
     n = wl.T * wl.k
-    return 8192 < n <= 65536 and wl.E >= 128 and 19 * (wl.E + 1) * 4 <= 65536
+    c = 8 if wl.E < 128 else 1
+    return 8192 < n <= 65536 and wl.E >= 32 and (2 * c + 17) * (wl.E + 1) * 4 <= 65536
 
 
 def combine_kernel_name(wl, ncu):

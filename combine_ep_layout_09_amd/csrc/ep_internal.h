@@ -54,7 +54,7 @@ constexpr int64_t kFusedMaxVisits = int64_t{1} << 23;
 // Mid-size tables (kFusedMaxEntries < T*k <= kWholeMaxEntries, LDS for E):
 // ep_layout is one kernel in which every workgroup reads the whole table.
 constexpr int kWholeMaxEntries = 65536;
-constexpr int kWholeMinExperts = 128;
+constexpr int kWholeMinExperts = 32;
 bool layout_whole_fits(const ep_problem& p);
 hipError_t launch_layout(const ep_problem& p, const int32_t* topk_idx, const ep_layout_t& out,
                          int32_t* workspace, hipStream_t stream);

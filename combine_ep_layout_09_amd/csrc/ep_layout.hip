@@ -110,8 +110,14 @@ constexpr int kWholeThreads = 1024;
 constexpr int kWholeWaves = kWholeThreads / kWave;
 constexpr int kWholeQuadSteps = 8;  // table quads a lane has in flight
 
+// Copies of the two histograms: with few experts many lanes of one LDS
+// atomic instruction hit the same bin (skewed routing more so), and the
+// atomics to one address are applied one lane at a time; lane l counts into
+// copy l mod nc, and the copies are summed once the table is counted.
+__host__ __device__ inline int whole_copies(int E) { return E < 128 ? 8 : 1; }
+
 __host__ __device__ inline size_t whole_lds_words(int E) {
-    return static_cast<size_t>(3 + kWholeWaves) * (E + 1);
+    return static_cast<size_t>(2 * whole_copies(E) + 1 + kWholeWaves) * (E + 1);
 }
 
 __global__ __launch_bounds__(kWholeThreads) void layout_whole_kernel(
@@ -122,9 +128,10 @@ __global__ __launch_bounds__(kWholeThreads) void layout_whole_kernel(
     __shared__ int32_t s_wsum[kWholeWaves];
     __shared__ int32_t s_wover[kWholeWaves];
     const int W = E + 1;
-    int32_t* part = sm;           // [2][E+1]: ids before P0, the rest (bin E: invalid)
-    int32_t* off = sm + 2 * W;    // [E+1]
-    int32_t* wcnt = off + W;      // [waves][E+1]: own entries per expert of each wave
+    const int nc = whole_copies(E);
+    int32_t* part = sm;            // [nc][2][E+1]: ids before P0, the rest (bin E: invalid)
+    int32_t* off = sm + nc * 2 * W;  // [E+1]
+    int32_t* wcnt = off + W;       // [waves][E+1]: own entries per expert of each wave
 
     const int tid = static_cast<int>(threadIdx.x);
     const int lane = static_cast<int>(lane_id());
@@ -135,8 +142,8 @@ __global__ __launch_bounds__(kWholeThreads) void layout_whole_kernel(
     const bool has_own = i_own < n;
     // the own entry first: a wave's loads return in issue order
     const int32_t own_id = idx[has_own ? i_own : n - 1];
-    for (int e = tid; e < (2 + kWholeWaves) * W; e += kWholeThreads)
-        (e < 2 * W ? part[e] : wcnt[e - 2 * W]) = 0;
+    for (int e = tid; e < (2 * nc + kWholeWaves) * W; e += kWholeThreads)
+        (e < 2 * nc * W ? part[e] : wcnt[e - 2 * nc * W]) = 0;
     __syncthreads();
 
     // Own entries: rank among the lower lanes of the wave, and per-wave
@@ -151,6 +158,7 @@ __global__ __launch_bounds__(kWholeThreads) void layout_whole_kernel(
     // loads per lane in flight, then their counts.
     const int nq = n / 4;
     const int4* quads = reinterpret_cast<const int4*>(idx);
+    int32_t* mypart = part + (lane & (nc - 1)) * 2 * W;
     for (int q0 = 0; q0 < nq; q0 += kWholeQuadSteps * kWholeThreads) {
         int4 g[kWholeQuadSteps];
 #pragma unroll
@@ -164,7 +172,7 @@ __global__ __launch_bounds__(kWholeThreads) void layout_whole_kernel(
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const int32_t id = id4[c];
-                    atomicAdd(&part[(valid_id(id, E) ? id : E) + (4 * qi + c < P0 ? 0 : W)], 1);
+                    atomicAdd(&mypart[(valid_id(id, E) ? id : E) + (4 * qi + c < P0 ? 0 : W)], 1);
                 }
             }
         }
@@ -172,9 +180,17 @@ __global__ __launch_bounds__(kWholeThreads) void layout_whole_kernel(
     if (tid < n - 4 * nq) {  // the last n % 4 ids
         const int i = 4 * nq + tid;
         const int32_t id = idx[i];
-        atomicAdd(&part[(valid_id(id, E) ? id : E) + (i < P0 ? 0 : W)], 1);
+        atomicAdd(&mypart[(valid_id(id, E) ? id : E) + (i < P0 ? 0 : W)], 1);
     }
     __syncthreads();
+    if (nc > 1) {  // uniform
+        for (int e = tid; e < 2 * W; e += kWholeThreads) {
+            int32_t sum = part[e];
+            for (int c = 1; c < nc; ++c) sum += part[c * 2 * W + e];
+            part[e] = sum;
+        }
+        __syncthreads();
+    }
 
     // Offsets: exclusive scan of the totals over experts (E <= 1024: one lane
     // per expert), and the entries the capacity drops.
@@ -295,13 +311,15 @@ static_assert(kTableStride == 64, "kMaxLayoutWorkspaceBytes assumes 64-row table
 
 bool layout_whole_fits(const ep_problem& p) {
     const int64_t n = static_cast<int64_t>(p.num_tokens) * p.num_topk;
-    // Few experts put many lanes of one LDS atomic instruction on the same
-    // histogram bin (more so with skewed routing), and every workgroup counts
-    // the whole table: below 128 experts, and past 65536 entries, the
-    // histogram and ranking kernels are faster (measured: the skewed
-    // 8192 x 6 table over 64 experts, 12.5 us against 4.6 + 5.6 us; 16384 x 8
-    // over 256 experts, about 16 against 15 us; 4096 x 8 over 256 experts,
-    // about 8 against 12 us, event-timed).
+    // Every workgroup counts the whole table, so past 65536 entries the
+    // histogram and ranking kernels are faster (16384 x 8 over 256 experts:
+    // about 16 against 15 us; 4096 x 8: about 8 against 12 us, event-timed).
+    // Below 128 experts the histograms need their copies (one copy: the
+    // skewed 8192 x 6 table over 64 experts took 12.5 us against 4.6 + 5.6 us
+    // for the two kernels); with 8 copies the FP8 layout + dispatch call of
+    // that table is 61.6-62.6 against 63.0-63.7 us, also about 1 us faster at
+    // 32 and 96 experts, and 0.4 us slower at 16 (event-timed, the benchmark's
+    // order of calls).
     return n > kFusedMaxEntries && n <= kWholeMaxEntries && p.num_experts >= kWholeMinExperts &&
            whole_lds_words(p.num_experts) * 4 <= 65536;
 }

@@ -381,16 +381,23 @@ def test_duplicate_and_invalid_ids_large_table():
 
 def test_whole_table_layout_ids_and_tails():
     """The one-kernel layout of mid-size tables (8192 < T*k <= 65536, at
-    least 128 experts: every workgroup reads the whole table) through
+    least 32 experts: every workgroup reads the whole table) through
     ep_layout: duplicate ids in a row, ids outside [0, E), a run of one
     expert across tokens, tokens without a valid entry, with and without
     capacity (overflow included), tables whose length is not a multiple of 4
-    (the last ids are read one by one), and the same id mix on a larger
-    table that takes the two-kernel layout."""
+    (the last ids are read one by one), fewer than 128 experts (the
+    histograms counted in 8 copies; a third of the ids on one hot expert in
+    the skewed cases), and the same id mix on a larger table that takes the
+    two-kernel layout."""
     rng = np.random.default_rng(12)
-    for T, k, E, cap in ((3000, 8, 160, 0), (3000, 8, 160, 100), (3001, 7, 130, 0),
-                         (4681, 14, 256, 0), (16384, 8, 256, 600)):
+    for T, k, E, cap, hot in ((3000, 8, 160, 0, False), (3000, 8, 160, 100, False),
+                              (3001, 7, 130, 0, False), (4681, 14, 256, 0, False),
+                              (3001, 7, 64, 0, True), (3000, 8, 32, 300, True),
+                              (6000, 6, 127, 0, False), (8000, 8, 40, 0, True),
+                              (16384, 8, 256, 600, False)):
         ids = rng.integers(0, E, size=(T, k))
+        if hot:
+            ids[rng.random((T, k)) < 0.33] = E // 3
         ids[::7, 1] = ids[::7, 0]
         ids[::11, 2] = -1
         ids[::13, 3] = E
@@ -398,7 +405,7 @@ def test_whole_table_layout_ids_and_tails():
         ids[100:140] = 5
         ids[200:203] = -1
         H = 128 if T * k > 65536 else 256
-        c = _random_case(T, H, k, E, cap, False, seed=T + cap, ids=ids,
+        c = _random_case(T, H, k, E, cap, False, seed=T + cap + E, ids=ids,
                          name=f"whole_layout_T{T}_k{k}_E{E}_cap{cap}")
         got = run_gpu(c)
         check_case(c, got)
