@@ -239,7 +239,8 @@ def persistent_launch(wl, ncu):
     if own > 1024:
         return False
     rw = -(-own // 64)
-    head = ((3 + rw) * (wl.E + 1) + 3) & ~3
+    copies = 8 if wl.E < 128 else 1  # histogram copies below 128 experts
+    head = ((2 * copies + 1 + rw) * (wl.E + 1) + 3) & ~3
     return (head + maxtok * ((wl.k + 3) & ~3)) * 4 <= 65536
 
 

@@ -103,25 +103,38 @@ struct PersistParams {
 };
 
 // Dynamic LDS (int32 words):
-//   part [2][E+1]   part[0]: ids ahead of the workgroup's first entry,
-//                   part[1]: the others; bin E counts ids outside [0, E)
+//   part [nc][2][E+1]  part[0]: ids ahead of the workgroup's first entry,
+//                   part[1]: the others; bin E counts ids outside [0, E);
+//                   nc copies, lane l counting into copy l mod nc, summed
+//                   into copy 0 once the table is counted
 //   off  [E+1]      exclusive scan over experts of part[0] + part[1]
 //   wcnt [rw][E+1]  own entries per expert of each ranking wave
 //   slot [maxtok][kp] receive rows of each own token, rows padded to kp =
 //                   k rounded up to 4 words (16-byte aligned rows)
 __host__ __device__ inline int slot_stride(int k) { return (k + 3) & ~3; }
 
+// Copies of the histograms: with few experts many lanes of one LDS atomic
+// instruction hit the same bin (skewed routing more so), and the atomics to
+// one address are applied one lane at a time.
+__host__ __device__ inline int persist_copies(int E) { return E < 128 ? 8 : 1; }
+
+__host__ __device__ inline size_t persist_head_words(int E, int rw) {
+    const size_t head = static_cast<size_t>(2 * persist_copies(E) + 1 + rw) * (E + 1);
+    return (head + 3) & ~static_cast<size_t>(3);
+}
+
 __host__ __device__ inline size_t persist_lds_words(int E, int rw, int maxtok, int k) {
-    const size_t head = static_cast<size_t>(3 + rw) * (E + 1);
-    return ((head + 3) & ~static_cast<size_t>(3)) + static_cast<size_t>(maxtok) * slot_stride(k);
+    const size_t head = persist_head_words(E, rw);
+    return head + static_cast<size_t>(maxtok) * slot_stride(k);
 }
 
 // The workgroup's view of the problem: its run of chunks and tokens and its
 // LDS tables.
 struct Part {
-    int tid, lane, wave, b, E, k, kp, W;
+    int tid, lane, wave, b, E, k, kp, W, nc;
     int c_begin, c_end, tA, P0, n_own;
     int32_t* part;
+    int32_t* mypart;  // this lane's copy of part
     int32_t* off;
     int32_t* wcnt;
     int32_t* s_slot;
@@ -139,10 +152,12 @@ __device__ __forceinline__ Part make_part(const PersistParams& p, int32_t* s_dyn
     w.k = K > 0 ? K : p.k;
     w.kp = slot_stride(w.k);
     w.W = w.E + 1;
+    w.nc = persist_copies(w.E);
     w.part = s_dyn;
-    w.off = w.part + 2 * w.W;
+    w.mypart = w.part + (w.lane & (w.nc - 1)) * 2 * w.W;
+    w.off = w.part + 2 * w.nc * w.W;
     w.wcnt = w.off + w.W;
-    w.s_slot = s_dyn + ((static_cast<size_t>(3 + p.rw) * w.W + 3) & ~static_cast<size_t>(3));
+    w.s_slot = s_dyn + persist_head_words(w.E, p.rw);
     const int all_chunks = p.T * p.C;  // < 2^31: at most CUs * 16 * kHoldFp8 here
     w.c_begin = w.b * kWaves * p.Q;
     w.c_end = min(w.c_begin + kWaves * p.Q, all_chunks);
@@ -164,9 +179,28 @@ __device__ __forceinline__ void count_quad(const Part& w, int nq, const int4& g,
         for (int c = 0; c < 4; ++c) {
             const int32_t id = id4[c];
             const int bin = (valid_id(id, w.E) ? id : w.E) + (4 * qi + c < w.P0 ? 0 : w.W);
-            atomicAdd(&w.part[bin], 1);
+            atomicAdd(&w.mypart[bin], 1);
         }
     }
+}
+
+// Zeroes the histogram copies and the per-wave counts (a barrier follows).
+__device__ __forceinline__ void zero_tables(const Part& w, int rw) {
+    const int parts = 2 * w.nc * w.W;
+    for (int e = w.tid; e < parts + rw * w.W; e += kThreads)
+        (e < parts ? w.part[e] : w.wcnt[e - parts]) = 0;
+}
+
+// After the table is counted (barrier before): the copies summed into copy 0.
+// Ends with a barrier when there is more than one copy.
+__device__ __forceinline__ void merge_copies(const Part& w) {
+    if (w.nc == 1) return;  // uniform
+    for (int e = w.tid; e < 2 * w.W; e += kThreads) {
+        int32_t sum = w.part[e];
+        for (int c = 1; c < w.nc; ++c) sum += w.part[c * 2 * w.W + e];
+        w.part[e] = sum;
+    }
+    __syncthreads();
 }
 
 // Own entries: rank among the same wave's lower lanes, and per-wave counts
@@ -327,8 +361,7 @@ void layout_dispatch_persistent_kernel(PersistParams p) {
         cid[j] = mine ? c : -1;
     }
 
-    for (int e = tid; e < (2 + p.rw) * w.W; e += kThreads)
-        (e < 2 * w.W ? w.part[e] : w.wcnt[e - 2 * w.W]) = 0;
+    zero_tables(w, p.rw);
     __syncthreads();
 
     // 2. Histograms of the table, split at the workgroup's first entry, and
@@ -337,6 +370,7 @@ void layout_dispatch_persistent_kernel(PersistParams p) {
     for (int u = 0; u < kIdQuads; ++u) count_quad(w, nq, q[u], u * kThreads + tid);
     const int32_t below = rank_own(w, p.rw, own_id);
     __syncthreads();
+    merge_copies(w);
 
     // 3. Offsets, slots and the layout outputs.
     finish_layout(p, w, own_id, below, s_wsum, s_wover);
@@ -419,14 +453,14 @@ void layout_dispatch_persistent_fp8_kernel(PersistParams p) {
         cid[j] = mine ? c : -1;
     }
 
-    for (int e = tid; e < (2 + p.rw) * w.W; e += kThreads)
-        (e < 2 * w.W ? w.part[e] : w.wcnt[e - 2 * w.W]) = 0;
+    zero_tables(w, p.rw);
     __syncthreads();
 
 #pragma unroll
     for (int u = 0; u < kIdQuads; ++u) count_quad(w, nq, q[u], u * kThreads + tid);
     const int32_t below = rank_own(w, p.rw, own_id);
     __syncthreads();
+    merge_copies(w);
 
     finish_layout(p, w, own_id, below, s_wsum, s_wover);
 
