@@ -90,14 +90,14 @@ __device__ __forceinline__ float row16_max(float m) {
 // come from one IEEE reciprocal per piece instead: r = fl(1 / scale) and
 // p = fl(f * r) carry two roundings of relative error <= 2^-24 each, so p
 // lies within 3 * 2^-24 |f / scale| of q = fl(f / scale), inside the interval
-// [p (1 - 2^-21), p (1 + 2^-21)] even after the rounding of its two ends.
-// Round-to-nearest-even onto E4M3 is monotone in the value, so where both
-// ends of that interval have the same code, q has it too (this holds at
+// between p (1 - 2^-21) and p (1 + 2^-21) even after the rounding of its two
+// ends.  Round-to-nearest-even onto E4M3 is monotone in the value, so where
+// both ends of that interval have the same code, q has it too (this holds at
 // zero, where the interval is a point, and for fp32-subnormal quotients,
-// whose codes are all a signed zero).  Each word of four channels whose end
-// codes differ in some byte -- a quotient next to a rounding midpoint --
-// and every channel when r is not finite (scale tiny) take the division
-// instead, in a branch a wave enters only when one of its lanes needs it.
+// whose codes are all a signed zero).  A channel whose two end codes differ
+// -- a quotient next to a rounding midpoint -- and every channel when r is
+// not finite (scale tiny) take the division instead, in a branch a wave
+// enters only when one of its lanes needs it.
 // Every value encoded here is below 464 in magnitude (|f| <= 448 * scale, and
 // the ends exceed p by less than 2^-20 relative), so no clamp is needed.
 __device__ __forceinline__ u32x2 quant8(const u32x4& w, float scale) {
