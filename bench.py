@@ -14,7 +14,10 @@ algorithmic bytes of dispatch (layout included) plus combine, divided by the
 mean step time over K steps, each run after a cache flush (a 512 MiB fill
 and a 1 GiB read, outside the timing) and timed by one HIP event pair on the
 kernels' stream.  The same K steps back to back with warm caches are in
-detail.warm_back_to_back.  `roofline` reports the dominant call against the
+detail.warm_back_to_back, and 20 steps captured in a HIP graph and replayed
+back to back in detail.graph_back_to_back (what a serving loop that cannot
+afford the host's per-call launch work sees).  `roofline` reports the
+dominant call against the
 8 TB/s HBM peak, its duration measured by HIP events around each call over
 K more flushed steps (a call of ep_layout_dispatch is one to three kernels:
 it is reported as a unit).  detail.configs times workloads 1-5 the same way.
@@ -398,22 +401,32 @@ def run_steps(ep, torch, wl, prob, fused, K, W, flush, eo_host=None, per_call=Tr
 
     out = dict(count=count, flushed=stats_ms(flushed))
     if per_call:
-        ev = HipEvents(4 * K)
+        # events before, between and after the calls (ep_layout has its own
+        # pair only on the separate path: an empty pair costs a few us)
+        n = 3 if fused else 4
+        ev = HipEvents(n * K)
         for i in range(K):
             flush()
-            ev.record(4 * i, sh)
-            do_layout(stream)
-            ev.record(4 * i + 1, sh)
+            e = n * i
+            ev.record(e, sh)
+            if not fused:
+                do_layout(stream)
+                e += 1
+                ev.record(e, sh)
             do_dispatch(stream)
-            ev.record(4 * i + 2, sh)
+            ev.record(e + 1, sh)
             do_combine(stream)
-            ev.record(4 * i + 3, sh)
+            ev.record(e + 2, sh)
         torch.cuda.synchronize()
 
         def mean_ms(a, b):
-            return sum(ev.elapsed_ms(4 * i + a, 4 * i + b) for i in range(K)) / K
+            return sum(ev.elapsed_ms(n * i + a, n * i + b) for i in range(K)) / K
 
-        out.update(layout_ms=mean_ms(0, 1), dispatch_ms=mean_ms(1, 2), combine_ms=mean_ms(2, 3))
+        if fused:
+            out.update(layout_ms=0.0, dispatch_ms=mean_ms(0, 1), combine_ms=mean_ms(1, 2))
+        else:
+            out.update(layout_ms=mean_ms(0, 1), dispatch_ms=mean_ms(1, 2),
+                       combine_ms=mean_ms(2, 3))
         ev.close()
 
     torch.cuda.synchronize()
@@ -422,8 +435,49 @@ def run_steps(ep, torch, wl, prob, fused, K, W, flush, eo_host=None, per_call=Tr
         step()
     torch.cuda.synchronize()
     out["warm_ms"] = (time.perf_counter() - t0) / K * 1e3
+
+    def step_on(s):
+        do_layout(s)
+        do_dispatch(s)
+        do_combine(s)
+
+    out["graph_ms"] = graph_step_ms(torch, step_on)
     del d
     return out
+
+
+def graph_step_ms(torch, step_on, G=20, R=10):
+    """Back-to-back steps replayed from a HIP graph: G steps captured once
+    (on a side stream, after one eager warm-up step there), the graph
+    replayed R times in a row on the current stream and timed by one HIP
+    event pair; returns ms per step.  The calls allocate nothing and issue
+    no memset, so the graph holds only the library's kernel launches; what
+    it removes is the host's per-call launch work, which the eager
+    back-to-back loop pays for small batches."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step_on(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for _ in range(G):
+            step_on(side)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    sh = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents(2)
+    ev.record(0, sh)
+    for _ in range(R):
+        g.replay()
+    ev.record(1, sh)
+    torch.cuda.synchronize()
+    ms = ev.elapsed_ms(0, 1) / (R * G)
+    ev.close()
+    del g
+    return ms
 
 
 def skew_sweep(ep, torch, workloads, args, flush):
@@ -452,7 +506,7 @@ def skew_sweep(ep, torch, workloads, args, flush):
                        "topk": wl.k, "payload": "e4m3" if wl.fp8 else "bf16", **over,
                        "hot_load_ratio": wl.meta.get("hot_load_ratio")},
             "max_over_mean_expert_load": round(float(counts.max() / counts.mean()), 3),
-            "us_per_call": {"layout": round(r["layout_ms"] * 1e3, 3),
+            "us_per_call": {"layout": round(r["layout_ms"] * 1e3, 3) if args.path != "fused" else None,
                             "dispatch": round(r["dispatch_ms"] * 1e3, 3),
                             "combine": round(r["combine_ms"] * 1e3, 3)},
         }), flush=True)
@@ -488,7 +542,11 @@ def config_table(ep, torch, workloads, args, flush, ue8m0):
                         "us_max": round(r["flushed"]["max"] * 1e3, 2)},
             "warm": {"us_per_step": round(w * 1e3, 2), "GBps": round(gbps(w), 1),
                      "pct_of_hbm_peak": round(100 * gbps(w) / HBM_PEAK_GBPS, 2)},
-            "us_per_call_flushed": {"layout": round(r["layout_ms"] * 1e3, 2),
+            "graph": {"us_per_step": round(r["graph_ms"] * 1e3, 2),
+                      "GBps": round(gbps(r["graph_ms"]), 1),
+                      "pct_of_hbm_peak": round(100 * gbps(r["graph_ms"]) / HBM_PEAK_GBPS, 2)},
+            "us_per_call_flushed": {"layout": round(r["layout_ms"] * 1e3, 2)
+                                    if args.path != "fused" else None,
                                     "dispatch": round(r["dispatch_ms"] * 1e3, 2),
                                     "combine": round(r["combine_ms"] * 1e3, 2)},
         }
@@ -628,10 +686,14 @@ def main():
             "warm_back_to_back": {"us_per_step": round(r["warm_ms"] * 1e3, 3),
                                   "GBps": round(warm_gbps, 2),
                                   "pct_of_hbm_peak": round(100 * warm_gbps / HBM_PEAK_GBPS, 2)},
-            "us_per_call_flushed": {"layout": round(layout_ms * 1e3, 3),
+            "us_per_call_flushed": {"layout": round(layout_ms * 1e3, 3) if not fused else None,
                                     "dispatch": round(dispatch_ms * 1e3, 3),
                                     "dispatch_incl_layout": round((layout_ms + dispatch_ms) * 1e3, 3),
                                     "combine": round(combine_ms * 1e3, 3)},
+            "graph_back_to_back": {"us_per_step": round(r["graph_ms"] * 1e3, 3),
+                                   "GBps": round(total_bytes / r["graph_ms"] * 1e3 / 1e9, 2),
+                                   "pct_of_hbm_peak": round(
+                                       100 * total_bytes / r["graph_ms"] * 1e3 / 1e9 / HBM_PEAK_GBPS, 2)},
             "GBps_per_call": {
                 "dispatch_incl_layout": round(nb["dispatch_total"] / ((layout_ms + dispatch_ms) / 1e3) / 1e9, 2),
                 "combine_kernel": round(nb["combine_kernel"] / (combine_ms / 1e3) / 1e9, 2)},
