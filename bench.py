@@ -367,8 +367,8 @@ def run_steps(ep, torch, wl, prob, fused, K, W, flush, eo_host=None, per_call=Tr
       calls:   K more flushed steps with an event before, between and after
                the calls (per-call durations; the middle event adds a small
                bubble, so the step time comes from `flushed`);
-      warm:    K steps back to back, nothing between them, wall time between
-               two device synchronisations."""
+      warm:    K steps back to back, nothing between them, one HIP event pair
+               around all K."""
     d = device_inputs(ep, torch, wl, prob, eo_host)
     lay = d["lay"]
     if fused:
@@ -436,11 +436,14 @@ def run_steps(ep, torch, wl, prob, fused, K, W, flush, eo_host=None, per_call=Tr
         ev.close()
 
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    ev = HipEvents(2)
+    ev.record(0, sh)
     for _ in range(K):
         step()
+    ev.record(1, sh)
     torch.cuda.synchronize()
-    out["warm_ms"] = (time.perf_counter() - t0) / K * 1e3
+    out["warm_ms"] = ev.elapsed_ms(0, 1) / K
+    ev.close()
 
     def step_on(s):
         do_layout(s)
