@@ -464,8 +464,13 @@ def run_steps(ep, torch, wl, prob, fused, K, W, flush, eo_host=None, per_call=Tr
     ev.close()
 
     nb = algorithmic_bytes(wl)
-    out.update(rotating_steps(ep, torch, wl, prob, fused, d, K,
-                              nb["dispatch_total"] + nb["combine_total"]))
+    step_bytes = nb["dispatch_total"] + nb["combine_total"]
+    if step_bytes >= (64 << 20):
+        out.update(rotating_steps(ep, torch, wl, prob, fused, d, K, step_bytes))
+    else:
+        # a step this small would need dozens of buffer sets; their
+        # allocations were seen to slow the larger workloads timed after them
+        out.update(rotating_ms=None, rotating_sets=None)
     del d
     return out
 
@@ -475,11 +480,9 @@ def rotating_steps(ep, torch, wl, prob, fused, d, K, step_bytes):
     buffer set i mod S -- S copies of every input and output at their own
     addresses, S chosen so that the other sets' traffic between two uses of
     one set is at least 1 GiB (4x the 256 MB MALL), within 16 GiB of buffers
-    and 3 to 64 sets -- timed by one HIP event pair around all K steps.  At
-    prefill sizes no step finds its inputs in a cache, and no per-step marker
-    or flush is in the timed region.  (Decode-sized steps touch little of
-    their fixed-capacity buffers, so fewer sets fit and the other sets'
-    traffic is smaller.)"""
+    and 3 to 64 sets -- timed by one HIP event pair around all K steps.  No
+    step finds its inputs in a cache, and no per-step marker or flush is in
+    the timed region.  Run for steps of at least 64 MiB only."""
     import math
     alloc = sum(t.numel() * t.element_size() for t in (
         d["idx"], d["w"], d["x"], d["eo"], d["recv_x"], d["y"],
@@ -631,10 +634,11 @@ def config_table(ep, torch, workloads, args, flush, ue8m0):
                         "us_max": round(r["flushed"]["max"] * 1e3, 2)},
             "warm": {"us_per_step": round(w * 1e3, 2), "GBps": round(gbps(w), 1),
                      "pct_of_hbm_peak": round(100 * gbps(w) / HBM_PEAK_GBPS, 2)},
-            "sustained_cold": {"us_per_step": round(r["rotating_ms"] * 1e3, 2),
-                               "GBps": round(gbps(r["rotating_ms"]), 1),
-                               "pct_of_hbm_peak": round(100 * gbps(r["rotating_ms"]) / HBM_PEAK_GBPS, 2),
-                               "buffer_sets": r["rotating_sets"]},
+            "sustained_cold": None if r["rotating_ms"] is None else {
+                "us_per_step": round(r["rotating_ms"] * 1e3, 2),
+                "GBps": round(gbps(r["rotating_ms"]), 1),
+                "pct_of_hbm_peak": round(100 * gbps(r["rotating_ms"]) / HBM_PEAK_GBPS, 2),
+                "buffer_sets": r["rotating_sets"]},
             "event_pair_overhead_us": round(r["empty_pair_ms"] * 1e3, 2),
             "graph": {"us_per_step": round(r["graph_ms"] * 1e3, 2),
                       "GBps": round(gbps(r["graph_ms"]), 1),
@@ -786,8 +790,8 @@ def main():
                      "avg_launch_us": round(dom_ms * 1e3, 3)},
         "detail": {
             "pct_of_hbm_peak": round(pct, 2),
-            "target": target_text(wl, pct, 100 * total_bytes / r["rotating_ms"] * 1e3 / 1e9
-                                  / HBM_PEAK_GBPS),
+            "target": target_text(wl, pct, None if r["rotating_ms"] is None else
+                                  100 * total_bytes / r["rotating_ms"] * 1e3 / 1e9 / HBM_PEAK_GBPS),
             "flushed_step_us": {k: round(v * 1e3, 3) for k, v in r["flushed"].items()},
             "warm_back_to_back": {"us_per_step": round(r["warm_ms"] * 1e3, 3),
                                   "GBps": round(warm_gbps, 2),
@@ -796,7 +800,7 @@ def main():
                                     "dispatch": round(dispatch_ms * 1e3, 3),
                                     "dispatch_incl_layout": round((layout_ms + dispatch_ms) * 1e3, 3),
                                     "combine": round(combine_ms * 1e3, 3)},
-            "sustained_cold": {
+            "sustained_cold": None if r["rotating_ms"] is None else {
                 "us_per_step": round(r["rotating_ms"] * 1e3, 3),
                 "GBps": round(total_bytes / r["rotating_ms"] * 1e3 / 1e9, 2),
                 "pct_of_hbm_peak": round(100 * total_bytes / r["rotating_ms"] * 1e3 / 1e9 / HBM_PEAK_GBPS, 2),
