@@ -379,6 +379,47 @@ def test_duplicate_and_invalid_ids_large_table():
         assert got["status"][0] == int(((ids < 0) | (ids >= E)).sum())
 
 
+CAP_SMALL = [
+    # (T, H, k, E, cap, fp8, hot, name): fixed capacity with at most 1024
+    # routing entries (decode batches): the one-kernel layout + dispatch
+    (128, 7168, 8, 256, 128, 1, False, "decode_shape"),
+    (100, 1024, 8, 12, 40, 1, True, "overflow_dup_invalid"),
+    (100, 1024, 8, 12, 40, 2, True, "overflow_dup_invalid_ue8m0"),
+    (100, 1024, 8, 12, 40, 0, True, "overflow_dup_invalid_bf16"),
+    (32, 4096, 32, 64, 12, 1, True, "k32_two_tokens_per_workgroup"),
+    (37, 2304, 7, 9, 20, 1, False, "table_259_entries_odd_k"),
+    (1, 128, 1, 1, 1, 1, False, "single_entry"),
+    (3, 8, 5, 1000, 2, 0, False, "few_tokens_many_experts"),
+    (170, 1920, 6, 33, 17, 2, True, "ragged_blocks_1020_entries"),
+    (128, 7168, 8, 256, 3, 1, True, "decode_shape_tiny_capacity"),
+]
+
+
+@pytest.mark.parametrize("spec", CAP_SMALL, ids=[c[-1] for c in CAP_SMALL])
+def test_capacity_small_tables(spec):
+    """Small routing tables with a fixed capacity through ep_layout_dispatch
+    (one kernel: workgroups that are not workgroup 0 count only the experts
+    whose empty rows they mark) and through ep_layout + ep_dispatch: every
+    layout array, receive row, scale and combine output against the oracle.  "hot": duplicate ids inside rows, ids outside
+    [0, E) (-1, E, 2^30), a run of one expert across tokens and one token
+    whose k entries are all one expert -- with capacities that drop entries."""
+    T, H, k, E, cap, fp8, hot, name = spec
+    rng = np.random.default_rng(zlib.crc32(name.encode()) % 1000)
+    ids = rng.integers(0, E, size=(T, k))
+    if hot:
+        ids[::7, min(1, k - 1)] = ids[::7, 0]
+        ids[::11, min(2, k - 1)] = -1
+        ids[::13, min(3, k - 1)] = E
+        ids[::17, 0] = 1 << 30
+        ids[T // 3:T // 3 + max(1, T // 10)] = E // 2
+        ids[T - 1] = 0
+    for fused in (True, False):
+        c = _random_case(T, H, k, E, cap, fp8, seed=cap + T, ids=ids, name=f"cap_small_{name}")
+        got = run_gpu(c, fused=fused)
+        check_case(c, got)
+        assert got["status"][0] == int(((ids < 0) | (ids >= E)).sum())
+
+
 def test_whole_table_layout_ids_and_tails():
     """The one-kernel layout of mid-size tables (8192 < T*k <= 65536, at
     least 32 experts: every workgroup reads the whole table) through
