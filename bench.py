@@ -14,10 +14,10 @@ algorithmic bytes of dispatch (layout included) plus combine, divided by the
 mean step time over K steps, each run after a cache flush (a 512 MiB fill
 and a 1 GiB read, outside the timing) and timed by one HIP event pair on the
 kernels' stream.  Beside it in `detail`:
-  sustained_cold      K steps back to back over rotating copies of every
-                      buffer (no step finds its inputs in a cache), one
-                      event pair around all K -- no flush or per-step
-                      marker inside the timed region;
+  sustained_cold      K steps back to back over rotating copies of the
+                      inputs and outputs (no step finds its inputs in a
+                      cache), one event pair around all K -- no flush or
+                      per-step marker inside the timed region;
   event_pair_overhead_us  an empty event pair after a flush: what the two
                       markers add to each flushed single step;
   warm_back_to_back   K steps back to back on one set of buffers;
@@ -476,53 +476,42 @@ def run_steps(ep, torch, wl, prob, fused, K, W, flush, eo_host=None, per_call=Tr
 
 
 def rotating_steps(ep, torch, wl, prob, fused, d, K, step_bytes):
-    """Sustained steps with cold inputs: K steps back to back, step i on
-    buffer set i mod S -- S copies of every input and output at their own
-    addresses, S chosen so that the other sets' traffic between two uses of
-    one set is at least 1 GiB (4x the 256 MB MALL), within 16 GiB of buffers
-    and 3 to 64 sets -- timed by one HIP event pair around all K steps.  No
-    step finds its inputs in a cache, and no per-step marker or flush is in
-    the timed region.  Run for steps of at least 64 MiB only."""
+    """Sustained steps with cold inputs: K steps back to back, timed by one
+    HIP event pair around all K, no flush or per-step marker inside.  Step i
+    reads input set i mod S_in (x, topk_idx, topk_weights) and uses buffer
+    set i mod S_out (expert outputs, layout, receive rows, y, workspace).
+    Most of a step's traffic is non-temporal and need not displace a plainly
+    loaded input from the 256 MB MALL, so the input sets alone must cycle
+    through at least 1 GiB between two uses of one (measured: with three
+    whole-step sets the skewed step's x stayed in the MALL, 131 against 141 us
+    with six or more); S_in = ceil(1 GiB / input bytes) + 1 (3 to 64), and
+    S_out = 3 (larger than the MALL together at these sizes)."""
     import math
-    alloc = sum(t.numel() * t.element_size() for t in (
-        d["idx"], d["w"], d["x"], d["eo"], d["recv_x"], d["y"],
-        d["lay"].slot_of, d["lay"].src_of_slot) if t is not None)
-    if d["recv_s"] is not None:
-        alloc += d["recv_s"].numel() * d["recv_s"].element_size()
-    # enough sets for 1 GiB of other traffic between two uses of one, within
-    # 16 GiB of buffers (at least 3 sets, at most 64)
-    sets_n = int(max(3, min(64, math.ceil((1 << 30) / max(step_bytes, 1)) + 1,
-                            (16 << 30) // max(alloc, 1))))
-    sets = [d]
-    for _ in range(sets_n - 1):
-        c = dict(idx=d["idx"].clone(), w=d["w"].clone(), x=d["x"].clone(), eo=d["eo"].clone())
-        c["lay"] = ep.Layout.empty(prob, "cuda")
-        c["ws"] = ep.alloc_workspace(prob, "cuda")
+    in_bytes = sum(t.numel() * t.element_size() for t in (d["idx"], d["w"], d["x"]))
+    s_in = int(max(3, min(64, math.ceil((1 << 30) / max(in_bytes, 1)) + 1)))
+    s_out = 3
+    ins = [d] + [dict(idx=d["idx"].clone(), w=d["w"].clone(), x=d["x"].clone())
+                 for _ in range(s_in - 1)]
+    outs = [d]
+    for _ in range(s_out - 1):
+        c = dict(eo=d["eo"].clone(), lay=ep.Layout.empty(prob, "cuda"),
+                 ws=ep.alloc_workspace(prob, "cuda"), y=torch.empty_like(d["y"]))
         c["recv_x"], c["recv_s"] = ep.alloc_recv(prob, "cuda")
-        c["y"] = torch.empty_like(d["y"])
-        sets.append(c)
-    calls = []
-    for c in sets:
-        if fused:
-            lay_call = None
-            disp = ep.prepare_layout_dispatch(prob, c["idx"], c["lay"], c["ws"], c["x"],
-                                              c["recv_x"], c["recv_s"])
-        else:
-            lay_call = ep.prepare_layout(prob, c["idx"], c["lay"], c["ws"])
-            disp = ep.prepare_dispatch(prob, c["x"], c["lay"], c["recv_x"], c["recv_s"])
-        comb = ep.prepare_combine(prob, c["eo"], c["lay"], c["w"], c["y"])
-        calls.append((lay_call, disp, comb))
+        outs.append(c)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
     def step(i):
-        lay_call, disp, comb = calls[i % sets_n]
-        if lay_call is not None:
-            lay_call(stream)
-        disp(stream)
-        comb(stream)
+        a, o = ins[i % s_in], outs[i % s_out]
+        if fused:
+            ep.ep_layout_dispatch(prob, a["idx"], o["lay"], o["ws"], a["x"], o["recv_x"],
+                                  o["recv_s"], stream=stream)
+        else:
+            ep.ep_layout(prob, a["idx"], o["lay"], o["ws"], stream=stream)
+            ep.ep_dispatch(prob, a["x"], o["lay"], o["recv_x"], o["recv_s"], stream=stream)
+        ep.ep_combine(prob, o["eo"], o["lay"], a["w"], o["y"], stream=stream)
 
-    for i in range(sets_n):
+    for i in range(max(s_in, s_out)):
         step(i)
     torch.cuda.synchronize()
     ev = HipEvents(2)
@@ -533,9 +522,9 @@ def rotating_steps(ep, torch, wl, prob, fused, d, K, step_bytes):
     torch.cuda.synchronize()
     ms = ev.elapsed_ms(0, 1) / K
     ev.close()
-    del sets, calls
+    del ins, outs
     torch.cuda.empty_cache()
-    return dict(rotating_ms=ms, rotating_sets=sets_n)
+    return dict(rotating_ms=ms, rotating_sets=s_in)
 
 
 def graph_step_ms(torch, step_on, G=20, R=10):
@@ -805,9 +794,9 @@ def main():
                 "GBps": round(total_bytes / r["rotating_ms"] * 1e3 / 1e9, 2),
                 "pct_of_hbm_peak": round(100 * total_bytes / r["rotating_ms"] * 1e3 / 1e9 / HBM_PEAK_GBPS, 2),
                 "buffer_sets": r["rotating_sets"],
-                "how": "K steps back to back, step i on buffer set i mod S (each set a copy of every "
-                       "input and output, the other sets moving >= 1 GiB between two uses of one), "
-                       "one HIP event pair around all K steps"},
+                "how": "K steps back to back, step i reading input set i mod S (x, topk_idx, "
+                       "topk_weights; S copies cycling through >= 1 GiB) and using output set i mod 3 "
+                       "(expert outputs, layout, receive rows, y), one HIP event pair around all K steps"},
             "event_pair_overhead_us": round(r["empty_pair_ms"] * 1e3, 3),
             "graph_back_to_back": {"us_per_step": round(r["graph_ms"] * 1e3, 3),
                                    "GBps": round(total_bytes / r["graph_ms"] * 1e3 / 1e9, 2),
