@@ -410,10 +410,15 @@ void layout_dispatch_persistent_kernel(PersistParams p) {
 }
 
 // FP8 rows.  The same layout; each chunk is quantised (one 128-channel block
-// per 16 lanes, as in the other dispatch kernels) and stored as soon as it
-// has arrived and the layout is known.  A wave's loads are all issued before
-// its first store, and the wait for a load does not wait for stores issued
-// after it, so quantising chunk j waits only for chunk j.
+// per 16 lanes, as in the other dispatch kernels) and stored once it has
+// arrived and the layout is known.  A wave's loads are all issued before its
+// first store.  Its stores sit under branches (an entry without a slot, the
+// lanes that write a scale), so where the paths meet the compiler counts
+// none of them, and quantising chunk j waits until at most 15 - j of the
+// wave's memory operations are in flight: for chunk j, and for most stores
+// of the chunks two and more before it.  That holds each wave to about two
+// chunks of stores in flight; branch-free stores with exact waits (a buffer
+// resource of size 0 where there is nothing to store) ran slower.
 //
 // UE8M0: power-of-two scales held as exponent bytes.
 template <int K, bool UE8M0>
