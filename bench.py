@@ -69,9 +69,20 @@ def algorithmic_bytes(wl, count=None, scale_bytes=4):
                 combine_kernel=combine_k, dispatch_total=b_disp, combine_total=b_comb)
 
 
+def _code_only(text):
+    """Source text without comments and with whitespace runs collapsed: what
+    the compiler sees (no string literal in these sources holds a comment
+    marker)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_digest(*names):
-    """Digest of kernel source files and every csrc header they include,
-    directly or not (quoted includes)."""
+    """Digest of the code (comments and layout aside) of kernel source files
+    and of every csrc header they include, directly or not (quoted
+    includes)."""
     csrc = os.path.join(ROOT, "combine_ep_layout_09_amd", "csrc")
     seen, todo = [], list(names)
     while todo:
@@ -84,8 +95,8 @@ def kernel_source_digest(*names):
                 todo.append(line.split('"')[1])
     h = hashlib.sha256()
     for f in sorted(seen):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f)) as fh:
+            h.update(f.encode() + b"\0" + _code_only(fh.read()).encode() + b"\0")
     return h.hexdigest()[:16]
 
 

@@ -99,7 +99,8 @@ def test_algorithmic_bytes_count_only_rows_that_get_a_slot():
 
 def test_source_digest_follows_included_headers(tmp_path, monkeypatch):
     """A counter summary is quoted only while its digest matches: the digest
-    covers the kernel file and every csrc header it includes."""
+    covers the code of the kernel file and of every csrc header it includes,
+    not their comments."""
     b = _bench()
     src = os.path.join(ROOT, "combine_ep_layout_09_amd", "csrc")
     fake_root = tmp_path / "root"
@@ -108,9 +109,11 @@ def test_source_digest_follows_included_headers(tmp_path, monkeypatch):
     d0 = b.kernel_source_digest("ep_fused_persist.hip")
     assert d0 == b.kernel_source_digest("ep_fused_persist.hip")
     hdr = fake_root / "combine_ep_layout_09_amd" / "csrc" / "ep_dispatch_dev.h"  # included by it
-    hdr.write_text(hdr.read_text() + "\n// changed\n")
+    hdr.write_text(hdr.read_text() + "\n// a comment\n/* and\n another */\n")
+    assert b.kernel_source_digest("ep_fused_persist.hip") == d0
+    hdr.write_text(hdr.read_text() + "\nconstexpr int kChanged = 1;\n")
     assert b.kernel_source_digest("ep_fused_persist.hip") != d0
     other = fake_root / "combine_ep_layout_09_amd" / "csrc" / "ep_combine.hip"  # not included
     d1 = b.kernel_source_digest("ep_fused_persist.hip")
-    other.write_text(other.read_text() + "\n// changed\n")
+    other.write_text(other.read_text() + "\nconstexpr int kChanged = 1;\n")
     assert b.kernel_source_digest("ep_fused_persist.hip") == d1
