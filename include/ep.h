@@ -1,7 +1,7 @@
 /* ep.h -- C ABI of libep: MoE token dispatch and combine on one AMD MI355X
  * (gfx950), every expert resident on this GPU.
  *
- * Three operations, each one or two hand-written HIP kernels launched
+ * Three operations, each one or more launches of hand-written HIP kernels,
  * asynchronously on the caller's stream:
  *
  *   ep_layout   routing table -> per-expert counts, expert-major offsets and a
@@ -210,7 +210,11 @@ int ep_layout_dispatch_noalloc(const ep_problem* prob, const int32_t* topk_idx,
  *   layout        as written by ep_layout (slot_of is read).
  *   topk_weights  fp32 [T, k], device; used as given (not renormalised).
  *   y             bf16 [T, H], device; every element is written.
- * Receive rows that no entry fills are never read. */
+ * Receive rows that no entry fills are never read.  Prefill-sized batches
+ * take one launch of one 1024-lane workgroup per CU per range of tokens that
+ * gives each wave at most 16 chunks of 64 16-byte pieces (up to 16 such
+ * launches, over consecutive token ranges); other batches one launch of a
+ * workgroup per (token, column tile). */
 int ep_combine(const ep_problem* prob, const void* expert_out, const ep_layout_t* layout,
                const float* topk_weights, void* y, void* stream);
 
