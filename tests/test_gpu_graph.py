@@ -8,9 +8,13 @@ replay, and eager work and synchronisations run between the replays.
 The captured calls allocate nothing (the layout workspace is the library's
 device array) and issue no memset, so the graph holds only the library's
 kernel launches.  Shapes: the decode workload (one layout+dispatch kernel,
-the per-token combine), the skewed workload (layout kernels, FP8 dispatch,
-persistent combine) and a 2048-token prefill (the one-launch layout +
-dispatch of one workgroup per CU)."""
+the per-token combine), the skewed workload (the one-kernel layout, FP8
+dispatch, persistent combine), a 2048-token prefill (the one-launch layout +
+dispatch of one workgroup per CU), and two forms whose kernels pass tables
+through the workspace array between launches: a 2047-token bf16 batch with
+k = 7 (the histogram kernel, then the ranking dispatch kernel) and the skewed
+shape over 16 experts (the histogram and ranking kernels of the layout, then
+the FP8 dispatch kernel)."""
 import numpy as np
 import pytest
 import torch
@@ -27,6 +31,8 @@ CASES = [
     ("skewed", dict(cid=4), 1),
     ("prefill_2048", dict(cid=3, T=2048), 0),
     ("decode_ue8m0", dict(cid=2), 2),
+    ("ranked_workspace", dict(cid=3, T=2047, k=7, H=2048), 0),
+    ("hist_rank_workspace", dict(cid=4, E=16), 1),
 ]
 
 

@@ -1,10 +1,15 @@
 """ep_layout_dispatch_noalloc (the library's fixed device array as the layout
 workspace) against ep_layout_dispatch with a caller-allocated workspace:
-every layout array, every receive row and every scale bit for bit, on two
-calls in a row, the second with a smaller problem.  Both problems take forms
-of the call that use the workspace: FP8 rows with k = 6 above 8192 routing
-entries (the layout kernels, then the dispatch kernel) and FP8 rows with
-k = 8 (the histogram kernel, then the ranking dispatch kernel)."""
+every layout array, every receive row and every scale bit for bit, on calls
+in a row, each smaller than the one before.  The first two take forms of the
+call that use the workspace -- FP8 rows with k = 6 over 16 experts (the
+histogram and ranking kernels of the layout, then the dispatch kernel) and
+FP8 rows with k = 8 (the histogram kernel, then the ranking dispatch
+kernel) -- which the test checks against bench.py's mirror of the library's
+launch rules; the decode workload (one kernel) does not touch it."""
+import importlib.util
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -16,6 +21,14 @@ import workloads
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _launch_rules():
+    spec = importlib.util.spec_from_file_location("bench_rules", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
 
 
 def _run(prob, idx, x, noalloc):
@@ -41,13 +54,19 @@ def _run(prob, idx, x, noalloc):
 
 def test_noalloc_matches_layout_dispatch():
     cases = [
-        # skewed workload: T=8192, H=4096, E=64, k=6, FP8, Zipf routing
-        (workloads.make(4), 1),
+        # skewed shape over 16 experts: T=8192, H=4096, k=6, FP8, Zipf routing
+        (workloads.make(4, E=16), 1),
         # a smaller problem with more experts and k = 8, UE8M0 scales
         (workloads.make(5, T=2000, H=1024, E=128), 2),
         # the decode workload (one kernel; the workspace is not touched)
         (workloads.make(2), 1),
     ]
+    rules = _launch_rules()
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert rules.fused_call_name(cases[0][0], ncu) == \
+        "layout_hist_kernel+layout_rank_kernel+dispatch_fp8_kernel"
+    assert rules.fused_call_name(cases[1][0], ncu) == \
+        "layout_hist_kernel+layout_dispatch_ranked_kernel"
     inputs, want = [], []
     for wl, mode in cases:
         prob = ep.Problem(wl.T, wl.H, wl.k, wl.E, wl.cap, mode)
