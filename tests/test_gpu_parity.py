@@ -210,10 +210,12 @@ EDGE = [
     dict(T=300, H=384, k=4, E=1, cap=0, fp8=True, name="one_expert"),
     dict(T=2500, H=256, k=6, E=7, cap=3, fp8=True, name="capacity_overflow"),
     dict(T=50, H=2304, k=4, E=16, cap=64, fp8=False, name="capacity_bf16_no_overflow"),
-    # routing tables around the size where the layout switches from one kernel
-    # to two (8192 entries), and a large two-pass table
+    # routing tables around the size where the layout leaves the small-table
+    # kernel (8192 entries): just above it the one-kernel whole-table layout
+    # (64 experts), or the histogram and ranking kernels where its LDS tables
+    # do not fit (1000 experts); and a large two-pass table
     dict(T=1024, H=128, k=8, E=64, cap=0, fp8=True, name="layout_single_pass_largest"),
-    dict(T=1025, H=136, k=8, E=64, cap=0, fp8=False, name="layout_two_pass_smallest"),
+    dict(T=1025, H=136, k=8, E=64, cap=0, fp8=False, name="layout_whole_table_smallest"),
     dict(T=1171, H=128, k=7, E=1000, cap=0, fp8=False, name="layout_two_pass_many_experts"),
     dict(T=40000, H=128, k=8, E=256, cap=1500, fp8=True, name="layout_two_pass_capacity"),
     # the largest table the one-kernel layout + dispatch takes (8192 entries),
@@ -251,10 +253,11 @@ EDGE = [
     dict(T=1700, H=2048, k=8, E=1024, cap=0, fp8=False, name="persistent_dispatch_max_experts"),
     dict(T=1024, H=4096, k=32, E=128, cap=0, fp8=False, name="persistent_dispatch_k32_largest_table"),
     dict(T=12000, H=512, k=2, E=1, cap=0, fp8=False, name="persistent_dispatch_one_expert"),
-    # FP8 rows at prefill sizes (8192 < T*k <= 49152 with at least one
+    # FP8 rows at prefill sizes (8192 < T*k <= 32768 with at least one
     # 64-piece chunk per wave: the one-launch form; else the multi-kernel
     # forms): rows of 15 blocks (a last chunk of 3 blocks), UE8M0 scales with
-    # capacity overflow, 49152 entries over 48 experts
+    # capacity overflow, 49152 entries over 48 experts (the one-kernel
+    # layout, then the dispatch kernel)
     dict(T=2000, H=1920, k=8, E=64, cap=0, fp8=1, name="prefill_fp8_ragged_blocks"),
     dict(T=3000, H=1024, k=6, E=32, cap=400, fp8=2, name="prefill_ue8m0_capacity_overflow"),
     dict(T=8192, H=4096, k=6, E=48, cap=0, fp8=1, name="prefill_fp8_k6_48_experts"),
@@ -354,9 +357,10 @@ def test_duplicate_and_invalid_ids():
 
 
 def test_duplicate_and_invalid_ids_large_table():
-    """The same id mix above 8192 entries (two-kernel layout; ranking inside
-    the dispatch kernel of ep_layout_dispatch at H = 256; one launch of one
-    workgroup per CU for bf16 rows at H = 640), with and without capacity,
+    """The same id mix above 8192 entries (ep_layout: the one-kernel
+    whole-table layout; ep_layout_dispatch: ranking inside the dispatch
+    kernel at H = 256, one launch of one workgroup per CU at H = 640, bf16 or
+    FP8 rows), with and without capacity,
     at a size the persistent combine takes (tokens with no valid entry
     included)."""
     rng = np.random.default_rng(10)
@@ -653,8 +657,8 @@ def test_fused_equals_separate_bitwise():
     """ep_layout_dispatch writes exactly what ep_layout + ep_dispatch write,
     receive rows and scales included, on the tiny and the decode workloads
     (small-table kernel), the prefill workload (one launch of one workgroup
-    per CU) and the skewed workload (FP8 with k = 6: the layout kernels and
-    the dispatch kernel)."""
+    per CU) and the skewed workload (FP8 with k = 6: the one-kernel layout,
+    then the dispatch kernel)."""
     for cid in (1, 2, 3, 4):
         c = Case.from_workload(workloads.make(cid))
         a = run_gpu(c)
