@@ -137,8 +137,9 @@ __global__ __launch_bounds__(kThreads) void layout_dispatch_small_kernel(SmallPa
         if (live[gq]) small::mark_entry(tab, E, tid, tab.ids[start[gq] + (tid - gq * k)]);
     }
     // count, offset and status come from workgroup 0; with fixed capacity the
-    // others need neither offsets nor the whole histogram
-    const bool totals = p.cap == 0 || b == 0;
+    // others need neither offsets nor the whole histogram (they build it only
+    // where that is cheaper than counting their own experts)
+    const bool totals = small::whole_histogram(p.cap, b, E, p.nwg);
     if (totals) small::histogram(tab, p.n, E);
     else small::count_experts(tab, p.n, E, b, p.nwg);
     __syncthreads();

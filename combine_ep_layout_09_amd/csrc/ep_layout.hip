@@ -69,8 +69,9 @@ __global__ __launch_bounds__(small::kThreads) void layout_small_kernel(
 
     if (tid < cnt) small::mark_entry(tab, E, tid, tab.ids[a + tid]);
     // count, offset and status come from workgroup 0; with fixed capacity the
-    // others need neither offsets nor the whole histogram
-    const bool totals = cap == 0 || b == 0;
+    // others need neither offsets nor the whole histogram (they build it only
+    // where that is cheaper than counting their own experts)
+    const bool totals = small::whole_histogram(cap, b, E, nwg);
     if (totals) small::histogram(tab, n, E);
     else small::count_experts(tab, n, E, b, nwg);
     __syncthreads();

@@ -171,7 +171,7 @@ __device__ __forceinline__ void count_run(const int32_t* __restrict__ idx, const
 
 // Everything after total, prior and num_invalid are in LDS and every ranking
 // wave has counted its run (all threads call it, after a barrier).
-__device__ void finish_layout(int b, const int32_t* __restrict__ idx, int64_t n, int E, int cap,
+__device__ void finish_layout(int b, const int32_t* __restrict__ idx, int E, int cap,
                               int nblocks, int64_t R, const RankLds& l, const Run& r,
                               const int32_t (&key)[kKeySteps], int32_t num_invalid,
                               int32_t* s_dropped, int32_t* __restrict__ count,
@@ -426,7 +426,7 @@ __device__ void rank_block(int b, int32_t* sm, const int32_t* __restrict__ idx, 
     }
     __syncthreads();
 
-    finish_layout(b, idx, n, E, cap, nblocks, R, l, r, key, s_invalid, &s_dropped, count, offset,
+    finish_layout(b, idx, E, cap, nblocks, R, l, r, key, s_invalid, &s_dropped, count, offset,
                   slot_of, src_of_slot, status);
 }
 

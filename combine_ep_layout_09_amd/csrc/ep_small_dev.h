@@ -109,6 +109,16 @@ __device__ inline void histogram(const Tables& t, int n, int E) {
     }
 }
 
+// Whether workgroup b builds the whole histogram (and the offsets): always
+// with the contiguous layout and in workgroup 0 (which writes count, offset
+// and status); otherwise only when it marks the empty rows of more than two
+// experts, since count_experts takes one pass over the table per expert and
+// the histogram one LDS add per id (decode: 448 workgroups over 256 experts
+// count; a 16-workgroup layout over 256 experts builds the histogram).
+__device__ inline bool whole_histogram(int cap, int b, int E, int nwg) {
+    return cap == 0 || b == 0 || E > 2 * nwg;
+}
+
 // With fixed capacity a workgroup other than workgroup 0 needs no offsets
 // (its slots are e*cap + rank) and, of the histogram, only the counts of the
 // experts whose empty rows it marks (b, b + nwg, ...): those are counted
