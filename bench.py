@@ -484,8 +484,7 @@ def run_steps(ep, torch, wl, prob, fused, K, W, flush, eo_host=None, per_call=Tr
     if rotating and step_bytes >= (64 << 20):
         out.update(rotating_steps(ep, torch, wl, prob, fused, d, K, step_bytes))
     else:
-        # a step this small would need dozens of buffer sets; their
-        # allocations were seen to slow the larger workloads timed after them
+        # a step this small would need dozens of buffer sets (up to 17 GB)
         out.update(rotating_ms=None, rotating_sets=None)
     del d
     return out
@@ -538,8 +537,10 @@ def rotating_steps(ep, torch, wl, prob, fused, d, K, step_bytes):
     torch.cuda.synchronize()
     ms = ev.elapsed_ms(0, 1) / K
     ev.close()
+    # the copies go back to torch's cache, not to the driver: for a few
+    # seconds after gigabytes are freed with hipFree, steps run about 2%
+    # slower (measured), which would fall on whatever is timed next
     del ins, outs
-    torch.cuda.empty_cache()
     return dict(rotating_ms=ms, rotating_sets=s_in)
 
 
@@ -616,11 +617,12 @@ def skew_sweep(ep, torch, workloads, args, flush):
 def config_table(args):
     """Every workload (1-5) timed the same ways as the headline (flushed,
     sustained cold, back to back, graph replay, per-call events), each in a
-    child process of its own running this script: in one process, the
-    gigabytes that an earlier workload's buffer sets allocate and free slowed
-    later steps by about 2%, on the same buffers too (skewed workload,
-    flushed: 143.4 against 140.0 us), while a fresh process measures a
-    workload as when it runs alone.  The parent does no GPU work meanwhile.
+    child process of its own running this script, so that each is measured
+    as when it runs alone: in one process, what one workload leaves behind
+    reaches the next (for a few seconds after gigabytes are returned to the
+    driver, steps run about 2% slower: skewed workload, flushed, 142.4-143.4
+    against 139.3-140.0 us, on the very same buffers).  The parent does no
+    GPU work meanwhile.
     A child that fails leaves an "error" entry; the rest are still timed."""
     import subprocess
     out = {}
@@ -766,7 +768,6 @@ def main():
     traffic = read_traffic(dom, dom_src, wl.name + ("_ue8m0" if ue8m0 else ""))
 
     copy_gbps = measure_copy_gbps(torch)
-    torch.cuda.empty_cache()
     configs = None if args.no_config_table else config_table(args)
     pct = 100 * value / HBM_PEAK_GBPS
 
