@@ -275,6 +275,7 @@ FUSED_SOURCES = {
     "layout_hist_kernel+layout_dispatch_ranked_kernel": ("ep_fused.hip", "ep_layout.hip"),
     "layout_hist_kernel+layout_rank_kernel+dispatch_fp8_kernel": ("ep_layout.hip", "ep_dispatch.hip"),
     "layout_whole_kernel+dispatch_fp8_kernel": ("ep_layout.hip", "ep_dispatch.hip"),
+    "layout_small_kernel+dispatch_fp8_kernel": ("ep_layout.hip", "ep_dispatch.hip"),
 }
 
 
@@ -290,6 +291,8 @@ def fused_call_name(wl, ncu):
         return "layout_dispatch_persistent_fp8_kernel" if wl.fp8 else "layout_dispatch_persistent_kernel"
     if not wl.fp8 or wl.k >= 8:
         return "layout_hist_kernel+layout_dispatch_ranked_kernel"
+    if wl.T * wl.k <= 8192:  # a small table over too many workgroups for one kernel
+        return "layout_small_kernel+dispatch_fp8_kernel"
     if whole_table_layout(wl):
         return "layout_whole_kernel+dispatch_fp8_kernel"
     return "layout_hist_kernel+layout_rank_kernel+dispatch_fp8_kernel"

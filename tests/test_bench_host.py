@@ -62,6 +62,11 @@ def test_launch_rule_mirror_on_the_five_workloads(cid, call, comb):
     (dict(fp8=True, T=16384, k=6), "layout_hist_kernel+layout_rank_kernel+dispatch_fp8_kernel"),
     # table length not a multiple of 4 stays off the one-launch form
     (dict(T=4095, k=7), "layout_hist_kernel+layout_dispatch_ranked_kernel"),
+    # a small table whose one-kernel form would visit too many ids (64 column
+    # tiles per token): FP8 with k < 8 takes the small-table layout kernel,
+    # bf16 the ranking dispatch
+    (dict(fp8=True, T=300, H=65536, k=4, E=64), "layout_small_kernel+dispatch_fp8_kernel"),
+    (dict(T=300, H=65536, k=4, E=64), "layout_hist_kernel+layout_dispatch_ranked_kernel"),
 ])
 def test_launch_rule_mirror_on_other_shapes(over, call):
     b = _bench()

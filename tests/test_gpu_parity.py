@@ -210,6 +210,13 @@ EDGE = [
     dict(T=300, H=384, k=4, E=1, cap=0, fp8=True, name="one_expert"),
     dict(T=2500, H=256, k=6, E=7, cap=3, fp8=True, name="capacity_overflow"),
     dict(T=50, H=2304, k=4, E=16, cap=64, fp8=False, name="capacity_bf16_no_overflow"),
+    # the largest hidden size (65536 channels, 512 blocks per row): bf16, FP8
+    # with capacity overflow, UE8M0 through the one-kernel form, and a batch
+    # that takes the persistent combine (128 chunks per row)
+    dict(T=20, H=65536, k=2, E=8, cap=0, fp8=False, name="max_hidden_bf16"),
+    dict(T=20, H=65536, k=2, E=8, cap=4, fp8=1, name="max_hidden_fp8_capacity"),
+    dict(T=300, H=65536, k=4, E=64, cap=0, fp8=2, name="max_hidden_ue8m0"),
+    dict(T=64, H=65536, k=2, E=8, cap=0, fp8=False, name="max_hidden_persistent_combine"),
     # routing tables around the size where the layout leaves the small-table
     # kernel (8192 entries): just above it the one-kernel whole-table layout
     # (64 experts), or the histogram and ranking kernels where its LDS tables
