@@ -346,6 +346,60 @@ def test_random_shapes(spec, fused):
     check_case(c, run_gpu(c, fused=fused))
 
 
+def _bench_rules():
+    """bench.py's mirror of the library's launch rules."""
+    import importlib.util
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "bench.py")
+    spec = importlib.util.spec_from_file_location("bench_rules", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _random_one_launch_shapes(n, seed=2027, ncu=256):
+    """Seeded random shapes that ep_layout_dispatch takes in one launch of one
+    workgroup per CU (8192 < T*k <= 32768, T*k a multiple of 4, between 1
+    and 14 (bf16) or 16 (FP8) chunks per wave): bf16 and both FP8 scale
+    formats, k from 1 to 32, 1 to 1024 experts, with and without capacity,
+    rows of any length the rule allows (ragged last chunks included).  The
+    launch form of each is checked against bench.py's mirror of the rules,
+    which the kernel traces confirm on the five workloads."""
+    from types import SimpleNamespace
+    rules = _bench_rules()
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        fp8 = int(rng.integers(0, 3))
+        k = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 8, 8, 12, 16, 32]))
+        n_ent = int(rng.integers(8193, 32769)) // 4 * 4
+        if n_ent % k:
+            continue
+        T = n_ent // k
+        E = int(rng.choice([1, 7, 32, 64, 100, 256, 1024]))
+        cap = 0 if rng.random() < 0.7 else int(rng.integers(1, max(2, 2 * T * k // E + 2)))
+        unit = 128 if fp8 else 8
+        H = int(rng.integers(1, 7168 // unit + 1)) * unit
+        R = T * k if cap == 0 else E * cap
+        wl = SimpleNamespace(T=T, H=H, k=k, E=E, cap=cap, fp8=bool(fp8), cid=0)
+        if R * H * 2 > 150e6 or not rules.persistent_launch(wl, ncu):
+            continue
+        out.append(dict(T=T, H=H, k=k, E=E, cap=cap, fp8=fp8,
+                        name=f"o{len(out)}_T{T}_H{H}_k{k}_E{E}_c{cap}_m{fp8}"))
+    return out
+
+
+ONE_LAUNCH_SHAPES = _random_one_launch_shapes(12)
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["separate", "fused"])
+@pytest.mark.parametrize("spec", ONE_LAUNCH_SHAPES, ids=[e["name"] for e in ONE_LAUNCH_SHAPES])
+def test_random_one_launch_shapes(spec, fused):
+    spec = dict(spec)
+    name = spec.pop("name")
+    c = _random_case(**spec, seed=zlib.crc32(name.encode()) % 1000, name=name)
+    check_case(c, run_gpu(c, fused=fused))
+
+
 def test_duplicate_and_invalid_ids():
     rng = np.random.default_rng(9)
     T, k, E = 700, 4, 12
